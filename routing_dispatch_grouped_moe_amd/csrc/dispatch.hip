@@ -1,0 +1,170 @@
+// Dispatch: a stable counting sort of the (token, k) pairs by expert, and the
+// copy of every token into its K expert rows (MoonEP page, step-by-step guide:
+// the S*K-rows contract and dispatch returning cu_seqlens with each token
+// written straight to its final row; MoE/MoD framework page, "What's in the
+// box", dispatch/combine item).
+//
+// gfx950 design, three launches, no atomics on the row order:
+//   1. bits:    one block per 256 tokens sets bit t of word [expert][t/32]
+//               in an LDS bitmap for every pair (order-free ds_or), then
+//               stores the bitmap and the per-expert popcounts.
+//   2. scan:    one block turns the [block, expert] counts into cu_seqlens
+//               and the first row of every (block, expert) run.
+//   3. scatter: one wavefront per token.  The rank of token s inside its
+//               expert's run is the popcount of the bitmap bits below s, so
+//               rows come out in ascending token order (bit-exact, unique).
+//               The wavefront then streams x[s] once in 16-byte pieces and
+//               writes each piece to the token's K rows (coalesced rows).
+#include "dev_common.h"
+#include "launch.h"
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kDispTok = 256;  // tokens per bitmap block (8 words of 32 bits)
+
+__global__ __launch_bounds__(256) void dispatch_bits_kernel(const int32_t* __restrict__ idx,
+                                                            uint32_t* __restrict__ bits_g,
+                                                            int32_t* __restrict__ hist_g,
+                                                            uint32_t* __restrict__ status, int S,
+                                                            int E, int K) {
+  extern __shared__ uint32_t bits[];  // [E][8]
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int i = tid; i < E * 8; i += 256) bits[i] = 0u;
+  __syncthreads();
+  const int s = b * kDispTok + tid;
+  uint32_t st = 0;
+  if (s < S) {
+    const uint32_t bit = 1u << (tid & 31);
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(int64_t)s * K + k];
+      if (e < 0 || e >= E) { st |= MOE_DEV_BAD_EXPERT; continue; }
+      const uint32_t old = atomicOr(&bits[e * 8 + (tid >> 5)], bit);
+      if (old & bit) st |= MOE_DEV_DUP_EXPERT;
+    }
+  }
+  if (st) atomicOr(status, st);
+  __syncthreads();
+  uint32_t* bo = bits_g + (size_t)b * E * 8;
+  for (int i = tid; i < E * 8; i += 256) bo[i] = bits[i];
+  for (int e = tid; e < E; e += 256) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c += __popc(bits[e * 8 + w]);
+    hist_g[(size_t)b * E + e] = c;
+  }
+}
+
+// Exclusive scan of up to 1024 ints held one per thread (blockDim.x == 1024).
+__device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  *total = sh[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ cu, int nb,
+                                                             int E) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = hist[(size_t)b * E + e];
+      base[(size_t)b * E + e] = tot;
+      tot += c;
+    }
+  }
+  int all;
+  const int start = block_exclusive_scan_1024(e < E ? tot : 0, sh, &all);
+  if (e < E) {
+    cu[e] = start;
+    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += start;
+  }
+  if (e == 0) cu[E] = all;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const void* __restrict__ x, const int32_t* __restrict__ idx,
+    const uint32_t* __restrict__ bits, const int32_t* __restrict__ base,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ tok_of, void* __restrict__ xd, int S,
+    int H, int E, int K) {
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= S) return;
+  const int b = s / kDispTok, t = s % kDispTok, wi = t >> 5;
+  int row = -1;
+  if (lane < K) {
+    const int e = idx[(int64_t)s * K + lane];
+    if (e >= 0 && e < E) {
+      const uint32_t* bw = bits + ((size_t)b * E + e) * 8;
+      int r = base[(size_t)b * E + e];
+      for (int w = 0; w < wi; ++w) r += __popc(bw[w]);
+      r += __popc(bw[wi] & ((1u << (t & 31)) - 1u));
+      row = r;
+      tok_of[row] = s;
+    }
+    row_of[(int64_t)s * K + lane] = row;
+  }
+  int rows[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) rows[k] = __shfl(row, k < K ? k : 0, kWave);
+  constexpr int kEl = BF16 ? 8 : 4;  // elements per 16-byte piece
+  const int pieces = H / kEl;
+  const u32x4* src = reinterpret_cast<const u32x4*>(
+      reinterpret_cast<const char*>(x) + (int64_t)s * H * (BF16 ? 2 : 4));
+  for (int c = lane; c < pieces; c += 64) {
+    const u32x4 v = src[c];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < K && rows[k] >= 0) {
+        u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(xd) +
+                                              (int64_t)rows[k] * H * (BF16 ? 2 : 4));
+        dst[c] = v;
+      }
+    }
+  }
+}
+
+void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
+                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
+                     int E, int K, bool bf16, hipStream_t s) {
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  int32_t* base = reinterpret_cast<int32_t*>(ws + L.base);
+  const int nb = L.nb;
+  if (nb > 0) {
+    TimedLaunch tl("dispatch_bits", s);
+    hipLaunchKernelGGL(dispatch_bits_kernel, dim3(nb), dim3(256), (size_t)E * 8 * 4, s, idx, bits,
+                       hist, status, (int)S, E, K);
+  }
+  {
+    TimedLaunch tl("dispatch_scan", s);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, hist, base, cu, nb, E);
+  }
+  if (S > 0) {
+    TimedLaunch tl("dispatch_scatter", s);
+    const int blocks = (int)((S + 3) / 4);
+    if (bf16)
+      hipLaunchKernelGGL(dispatch_scatter_kernel<true>, dim3(blocks), dim3(256), 0, s, x, idx, bits,
+                         base, row_of, tok_of, xd, (int)S, H, E, K);
+    else
+      hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3(blocks), dim3(256), 0, s, x, idx,
+                         bits, base, row_of, tok_of, xd, (int)S, H, E, K);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,96 @@
+// Internal host-side launch interface between the C ABI (api.hip) and the
+// kernel translation units.  Not exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Kernel timer hook: when the library timer is on, launches are bracketed by
+// events recorded on the launch stream.
+struct TimedLaunch {
+  TimedLaunch(const char* name, hipStream_t s);
+  ~TimedLaunch();
+  const char* name_;
+  hipStream_t stream_;
+  void* slot_;
+};
+
+// Workspace layout (bytes from the start of ws).  Every region is 256-byte aligned.
+struct WsLayout {
+  size_t status;      // uint32 device status word
+  size_t wgT;         // [Epad, H] router weight transposed (dtype)
+  size_t bits;        // dispatch: [nb, E, 8] uint32 token bitmaps (256 tokens per block)
+  size_t hist;        // dispatch: [nb, E] int32 per-block counts
+  size_t base;        // dispatch: [nb, E] int32 first row of each (block, expert)
+  size_t tiles;       // grouped GEMM: [max_tiles] int2 (expert, first row) per M tile
+  size_t ntiles;      // int32 number of valid M tiles
+  size_t dl_row;      // [R] fp32 dlogit of each dispatched row
+  size_t dwg_part;    // [dwg_splits, E, H] fp32 partial router-weight gradients
+  size_t total;
+  int nb;             // dispatch blocks of 256 tokens
+  int epad;           // E rounded up to 16
+  int max_tiles;      // upper bound on M tiles over all experts
+  int dwg_splits;     // row splits of the router-weight gradient
+};
+WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
+
+constexpr int kGemmBM = 128;  // M tile of the grouped GEMMs (rows per tile)
+
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16, hipStream_t s);
+void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,
+                  float* gates, int32_t* counts, uint32_t* status, int64_t S, int H, int E, int epad,
+                  int K, bool renorm, bool bf16, hipStream_t s);
+
+void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
+                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
+                     int E, int K, bool bf16, hipStream_t s);
+
+void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hipStream_t s);
+
+// Grouped GEMMs (see gemm.hip for the operand layouts).
+void launch_ffn_up(const void* xd, const int32_t* cu, const void* W1, const void* W3, void* h1,
+                   void* h3, void* a, int64_t R, int H, int Hf, int E, const WsLayout& L, char* ws,
+                   bool bf16, hipStream_t s);
+void launch_ffn_down(const void* a, const int32_t* cu, const void* W2, void* y, int64_t R, int H,
+                     int Hf, int E, const WsLayout& L, char* ws, bool bf16, hipStream_t s);
+void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void* h1,
+                   const void* h3, void* dh1, void* dh3, int64_t R, int H, int Hf, int E,
+                   const WsLayout& L, char* ws, bool bf16, hipStream_t s);
+void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const void* W1,
+                    const void* W3, void* dxd, int64_t R, int H, int Hf, int E, const WsLayout& L,
+                    char* ws, bool bf16, hipStream_t s);
+void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,
+                    int Hf, int E, bool accum, bool bf16, hipStream_t s);
+void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int32_t* cu,
+                     float* dW1, float* dW3, int64_t R, int H, int Hf, int E, bool accum,
+                     bool bf16, hipStream_t s);
+
+void launch_combine(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
+                    int H, int K, int64_t R, bool bf16, hipStream_t s);
+void launch_combine_bwd(const void* dout, const void* y, const int32_t* row_of,
+                        const int32_t* idx, const float* gates, void* dy, float* dgates,
+                        float* dlogits, float* dl_row, int64_t S, int H, int E, int K, int64_t R,
+                        bool bf16, hipStream_t s);
+void launch_dx(const void* dxd, const int32_t* row_of, const int32_t* idx, const float* dlogits,
+               const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R, bool bf16,
+               hipStream_t s);
+void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* dWg,
+                const WsLayout& L, char* ws, int64_t R, int H, int E, bool accum, bool bf16,
+                hipStream_t s);
+
+void launch_mod_select(int B, int T, int C, int H, bool bf16, const void* x, const void* w_r,
+                       float* r, int32_t* keep, void* xk, hipStream_t s);
+void launch_mod_merge(int B, int T, int C, int H, bool bf16, const void* x, const float* r,
+                      const int32_t* keep, const void* m, void* out, hipStream_t s);
+void launch_mod_backward(int B, int T, int C, int H, bool bf16, bool accum, const void* x,
+                         const void* w_r, const float* r, const int32_t* keep, const void* m,
+                         const void* dout, const void* dxk, void* dm, float* dr, void* dx,
+                         float* dw_r, float* part, hipStream_t s);
+constexpr int kModSplitsHost = 64;  // row splits of the MoD score-weight gradient
+
+}  // namespace moe

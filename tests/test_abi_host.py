@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, sizes its workspace, and rejects invalid arguments before launching."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from routing_dispatch_grouped_moe_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmoe_amd.so not built (python -m routing_dispatch_grouped_moe_amd.build)")
+    _lib.load()
+    return _lib
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert "moe_route" in names and "moe_backward" in names
+    lib = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_workspace_bytes_and_invalid_dims(L):
+    d = L.dims(8192, 7168, 2048, 384, 8, "bf16")
+    nb = L.moe_workspace_bytes(d)
+    assert nb > 0 and nb % 256 == 0
+    bad = [
+        L.dims(8, 100, 128, 8, 2, "bf16"),    # H not a multiple of 128
+        L.dims(8, 128, 128, 8, 9, "bf16"),    # K > E
+        L.dims(8, 128, 128, 2000, 2, "bf16"),  # E > 1024
+        L.dims(8, 128, 128, 64, 17, "bf16"),  # K > 16
+        L.dims(-1, 128, 128, 8, 2, "bf16"),
+        L.Dims(8, 128, 128, 8, 2, 7, 1),      # bad dtype
+        L.dims(1 << 28, 128, 128, 16, 16, "bf16"),  # S*K overflows int32
+    ]
+    for b in bad:
+        assert L.moe_workspace_bytes(b) == 0
+
+
+def _raw(L):
+    return L.load()
+
+
+FAKE = C.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
+MISALIGNED = C.c_void_p((1 << 20) + 4)
+
+
+def test_route_rejects_before_launch(L):
+    lib = _raw(L)
+    d = L.dims(64, 128, 256, 8, 2, "f32")
+    ws_n = L.moe_workspace_bytes(d)
+    args = [FAKE] * 7
+    # null x
+    st = lib.moe_route(C.byref(d), None, *args[1:], FAKE, ws_n, None)
+    assert st == 1
+    # misaligned topk_idx
+    st = lib.moe_route(C.byref(d), FAKE, FAKE, None, None, MISALIGNED, FAKE, FAKE, FAKE, ws_n, None)
+    assert st == 4
+    # workspace too small
+    st = lib.moe_route(C.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws_n - 256, None)
+    assert st == 5
+    # K > E
+    d2 = L.dims(64, 128, 256, 2, 3, "f32")
+    st = lib.moe_route(C.byref(d2), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws_n, None)
+    assert st == 6
+    # bad dtype
+    d3 = L.Dims(64, 128, 256, 8, 2, 5, 1)
+    st = lib.moe_route(C.byref(d3), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws_n, None)
+    assert st == 3
+    # null dims
+    st = lib.moe_route(None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws_n, None)
+    assert st == 1
+
+
+def test_other_entry_points_reject_before_launch(L):
+    lib = _raw(L)
+    d = L.dims(64, 128, 256, 8, 2, "bf16")
+    ws_n = L.moe_workspace_bytes(d)
+    assert lib.moe_dispatch(C.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws_n, None) == 1
+    assert lib.moe_grouped_ffn(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, 0, None) == 5
+    assert lib.moe_ffn_up(C.byref(d), FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, ws_n,
+                          None) == 4
+    assert lib.moe_ffn_down(C.byref(d), FAKE, None, FAKE, FAKE, FAKE, ws_n, None) == 1
+    assert lib.moe_combine(C.byref(d), FAKE, FAKE, None, FAKE, None) == 1
+    dshape = L.dims(64, 192, 256, 8, 2, "bf16")
+    assert lib.moe_combine(C.byref(dshape), FAKE, FAKE, FAKE, FAKE, None) == 6
+    # backward: raw (non-renormalised) gating is not implemented on the device
+    sv = L.Saved(*([1 << 20] * 15))
+    bb = L.BwdBufs(*([1 << 20] * 6))
+    draw = L.dims(64, 128, 256, 8, 2, "bf16", flags=0)
+    assert lib.moe_backward(C.byref(draw), C.byref(sv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            C.byref(bb), FAKE, ws_n, None) == 6
+    assert lib.moe_backward(C.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(bb), FAKE,
+                            ws_n, None) == 1
+    sv_bad = L.Saved(*([1 << 20] * 14 + [0]))
+    assert lib.moe_backward(C.byref(d), C.byref(sv_bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            C.byref(bb), FAKE, ws_n, None) == 1
+    # MoD
+    assert lib.moe_mod_select(4, 2048, 3000, 4096, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6
+    assert lib.moe_mod_select(4, 10000, 10, 4096, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6
+    assert lib.moe_mod_select(4, 2048, 1024, 4000, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6
+    assert lib.moe_mod_merge(0, 2048, 1024, 4096, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.moe_mod_backward(4, 2048, 1024, 4096, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 5
+    assert L.moe_mod_workspace_bytes(4096) > 0
+
+
+def test_status_strings(L):
+    lib = _raw(L)
+    for code, name in [(0, b"ok"), (5, b"workspace too small"), (7, b"HIP launch error")]:
+        assert lib.moe_status_string(code) == name

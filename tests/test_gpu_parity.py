@@ -1,0 +1,187 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integer outputs (top-K indices, counts, cu_seqlens, the permutation) must be
+bit-exact; xd must be a bitwise copy; float outputs are compared normwise
+(max |gpu - oracle| / max |oracle|) with 2e-2 for bf16 storage and 1e-5 for
+fp32 storage.  The top-K is checked against the oracle's selection on the
+GPU's own float32 logits (the logits themselves are checked to 1e-5: both
+sides accumulate the router product in at least fp32); everything downstream
+is the oracle's float64 arithmetic on the exact inputs and that routing.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_workload
+from tests.moe_testutil import (BF16_TOL, F32_TOL, assert_close, oracle_on_gpu_routing, to_dev,
+                                to_host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routing_dispatch_grouped_moe_amd import MoELayer  # noqa: E402
+from routing_dispatch_grouped_moe_amd import _lib as L  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True):
+    """Upload a workload, run the GPU forward (+ backward); return host copies."""
+    dt = wl.dtype
+    x = to_dev(wl.x, dt)
+    Wg = to_dev(wl.Wg, dt)
+    b = None if wl.bias is None else torch.from_numpy(wl.bias.astype(np.float32)).cuda()
+    W1 = to_dev(wl.W1, dt); W3 = to_dev(wl.W3, dt); W2 = to_dev(wl.W2, dt)
+    dout = to_dev(wl.dout, dt)
+    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt)
+    L.moe_clear_status(layer.ws)
+    layer.forward(x, Wg, b, W1, W3, W2)
+    if backward:
+        layer.backward(dout, x, Wg, W1, W3, W2)
+    torch.cuda.synchronize()
+    names = ["logits", "topk_idx", "gates", "counts", "cu", "row_of", "tok_of", "xd", "h1", "h3",
+             "a", "y", "out"]
+    if backward:
+        names += ["dy", "dh1", "dh3", "dxd", "dgates", "dlogits", "dx", "dWg", "dW1", "dW3", "dW2"]
+    got = {n: to_host(getattr(layer, n)) for n in names}
+    got["status"] = layer.status()
+    return got
+
+
+def check_against_oracle(wl, got, tol, backward=True):
+    x, Wg, bias = wl.x, wl.Wg, wl.bias
+    S, E, K = wl.S, wl.E, wl.K
+    # router logits: fp32 accumulation on both sides
+    want_logits = oracle.router_logits(x, Wg, bias)
+    assert_close("logits", got["logits"], want_logits, 1e-5)
+    fw, bw = oracle_on_gpu_routing(x, Wg, bias, wl.W1, wl.W3, wl.W2, K, got["logits"], wl.dout)
+    np.testing.assert_array_equal(got["topk_idx"], fw["idx"], err_msg="topk_idx")
+    assert_close("gates", got["gates"], fw["gates"], 1e-5)
+    np.testing.assert_array_equal(got["counts"], fw["counts"], err_msg="counts")
+    np.testing.assert_array_equal(got["cu"], fw["cu"], err_msg="cu_seqlens")
+    np.testing.assert_array_equal(got["row_of"], fw["row_of"], err_msg="row_of")
+    np.testing.assert_array_equal(got["tok_of"], fw["tok_of"], err_msg="tok_of")
+    np.testing.assert_array_equal(got["xd"], np.asarray(x, np.float32)[fw["tok_of"]], err_msg="xd")
+    errs = {}
+    for n in ("h1", "h3", "a", "y"):
+        errs[n] = assert_close(n, got[n], fw[n], tol)
+    errs["out"] = assert_close("out", got["out"], fw["out"], tol)
+    if backward:
+        for n, key in (("dy", "dy"), ("dgates", "dg"), ("dlogits", "dlogits"), ("dh1", "dh1"),
+                       ("dh3", "dh3"), ("dxd", "dxd"), ("dx", "dx"), ("dWg", "dWg"),
+                       ("dW1", "dW1"), ("dW3", "dW3"), ("dW2", "dW2")):
+            errs[n] = assert_close(n, got[n], bw[key], tol)
+    # end-to-end routing: the oracle's own logits vs the GPU's choice
+    own = oracle.topk_experts(want_logits, K)
+    flips = int(np.sum(np.any(own != got["topk_idx"], axis=1)))
+    return errs, flips
+
+
+CASES = [
+    # (id, config, overrides): reduced sizes span several tiles and ragged tails
+    ("c1_tiny_fp32", "c1", {}),
+    ("c2_mixtral_shape_small", "c2", dict(S=300, H=256, Hf=384)),
+    ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
+    ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
+    ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
+]
+
+
+@pytest.mark.parametrize("cid,cfg,ov", CASES, ids=[c[0] for c in CASES])
+def test_layer_parity(cid, cfg, ov):
+    _say(f"[parity] {cid} {ov}")
+    wl = make_workload(cfg, **ov, host_weights=True)
+    got = run_layer(wl)
+    tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
+    errs, flips = check_against_oracle(wl, got, tol)
+    _say(f"[parity] {cid} flips={flips} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert got["status"] == 0
+    if wl.dtype == "f32":
+        assert flips == 0
+
+
+def test_determinism_bitwise():
+    wl = make_workload("c3", S=257, H=256, Hf=256, host_weights=True)
+    a = run_layer(wl)
+    b = run_layer(wl)
+    for k in a:
+        if k == "status":
+            continue
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_uniform_logits_tie_break_and_empty_experts():
+    # Wg = 0 and no bias: every logit is exactly 0, so every token picks experts 0..K-1.
+    wl = make_workload("c2", S=150, H=256, Hf=256, E=8, K=3, host_weights=True)
+    wl.Wg[:] = 0.0
+    got = run_layer(wl)
+    assert (got["topk_idx"] == np.arange(3)[None, :]).all()
+    np.testing.assert_array_equal(got["counts"], [150, 150, 150, 0, 0, 0, 0, 0])
+    check_against_oracle(wl, got, BF16_TOL)
+    assert not np.any(got["dW1"][3:]) and not np.any(got["dW2"][3:])
+
+
+def test_single_token_and_one_hot_expert():
+    wl = make_workload("c2", S=1, H=128, Hf=128, E=4, K=2, host_weights=True)
+    got = run_layer(wl)
+    check_against_oracle(wl, got, BF16_TOL)
+    # every token forced onto expert 5 first: one expert owns S rows (many M tiles)
+    wl = make_workload("c3", S=700, H=128, Hf=256, host_weights=True)
+    wl.bias = np.zeros(wl.E, np.float32)
+    wl.bias[5] = 50.0
+    got = run_layer(wl)
+    assert (got["topk_idx"][:, 0] == 5).all()
+    check_against_oracle(wl, got, BF16_TOL)
+
+
+def test_single_expert_top1():
+    wl = make_workload("c2", S=130, H=128, Hf=256, E=1, K=1, host_weights=True)
+    got = run_layer(wl)
+    check_against_oracle(wl, got, BF16_TOL)
+    np.testing.assert_allclose(got["gates"], 1.0)
+
+
+def test_nonfinite_logit_sets_status():
+    wl = make_workload("c2", S=64, H=128, Hf=128, E=8, K=2, host_weights=True)
+    wl.x[3, 7] = np.inf
+    got = run_layer(wl, backward=False)
+    assert got["status"] & L.MOE_DEV_NONFINITE_LOGIT
+
+
+def test_dispatch_bad_expert_sets_status_and_skips_pair():
+    wl = make_workload("c2", S=64, H=128, Hf=128, E=8, K=2, host_weights=True)
+    layer = MoELayer(64, 128, 128, 8, 2, "bf16", backward=False)
+    L.moe_clear_status(layer.ws)
+    x = to_dev(wl.x, "bf16")
+    idx = np.tile(np.array([[1, 3]], np.int32), (64, 1))
+    idx[10, 1] = 8   # outside [0, E)
+    layer.topk_idx.copy_(torch.from_numpy(idx))
+    layer.dispatch(x)
+    torch.cuda.synchronize()
+    assert layer.status() & L.MOE_DEV_BAD_EXPERT
+    row_of = to_host(layer.row_of)
+    assert row_of[10 * 2 + 1] == -1
+    cu = to_host(layer.cu)
+    assert cu[-1] == 64 * 2 - 1 and cu[2] - cu[1] == 64 and cu[4] - cu[3] == 63
+
+
+def test_zero_tokens():
+    layer = MoELayer(0, 128, 128, 8, 2, "bf16")
+    W1 = torch.zeros(8, 128, 128, dtype=torch.bfloat16, device="cuda")
+    Wg = torch.zeros(128, 8, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(0, 128, dtype=torch.bfloat16, device="cuda")
+    layer.dW1.fill_(1.0)
+    layer.dWg.fill_(1.0)
+    layer.forward(x, Wg, None, W1, W1, W1)
+    layer.backward(x, x, Wg, W1, W1, W1)
+    torch.cuda.synchronize()
+    assert not to_host(layer.counts).any() and not to_host(layer.cu).any()
+    assert not to_host(layer.dW1).any() and not to_host(layer.dWg).any()
