@@ -248,7 +248,7 @@ def gate_backward(dg, logits, idx, renorm=True):
     return dl
 
 
-def expert_ffn_backward(dy, xd, cu, W1, W3, W2, h1, h3, a, experts=None):
+def expert_ffn_backward(dy, xd, cu, W1, W3, W2, h1, h3, a, experts=None, on_dW=None):
     """Per expert, with X its rows:
         da  = dy W2[e]^T
         dW2 = a^T dy
@@ -257,7 +257,10 @@ def expert_ffn_backward(dy, xd, cu, W1, W3, W2, h1, h3, a, experts=None):
         dxd = dh1 W1[e]^T + dh3 W3[e]^T
         dW1 = X^T dh1,  dW3 = X^T dh3
     Experts with no rows get zero gradients ([MEP] guide, fp32 gradient buffer
-    mirroring each projection tensor).
+    mirroring each projection tensor).  With ``on_dW`` given, each expert's
+    (dW1, dW3, dW2) is handed to on_dW(e, ...) instead of being stored (for
+    shapes whose gradients do not fit in host memory); the returned dW arrays
+    are then None.
     """
     dy = _f64(dy); xd = _f64(xd)
     E = len(cu) - 1
@@ -267,7 +270,11 @@ def expert_ffn_backward(dy, xd, cu, W1, W3, W2, h1, h3, a, experts=None):
     R = xd.shape[0]
     dxd = np.zeros((R, H)); dh1 = np.zeros((R, Hf)); dh3 = np.zeros((R, Hf))
     ex = list(range(E)) if experts is None else list(experts)
-    dW1 = np.zeros((len(ex), H, Hf)); dW3 = np.zeros((len(ex), H, Hf)); dW2 = np.zeros((len(ex), Hf, H))
+    if on_dW is None:
+        dW1 = np.zeros((len(ex), H, Hf)); dW3 = np.zeros((len(ex), H, Hf))
+        dW2 = np.zeros((len(ex), Hf, H))
+    else:
+        dW1 = dW3 = dW2 = None
     for i, e in enumerate(ex):
         r0, r1 = int(cu[e]), int(cu[e + 1])
         if r1 == r0:
@@ -275,13 +282,17 @@ def expert_ffn_backward(dy, xd, cu, W1, W3, W2, h1, h3, a, experts=None):
         X = xd[r0:r1]
         z = _f64(h1[r0:r1]); u = _f64(h3[r0:r1]); A = _f64(a[r0:r1]); D = dy[r0:r1]
         da = D @ get(W2, e).T
-        dW2[i] = A.T @ D
+        g2 = A.T @ D
         sg = 1.0 / (1.0 + np.exp(-z))
         dh1[r0:r1] = da * u * sg * (1.0 + z * (1.0 - sg))
         dh3[r0:r1] = da * (z * sg)
         dxd[r0:r1] = dh1[r0:r1] @ get(W1, e).T + dh3[r0:r1] @ get(W3, e).T
-        dW1[i] = X.T @ dh1[r0:r1]
-        dW3[i] = X.T @ dh3[r0:r1]
+        g1 = X.T @ dh1[r0:r1]
+        g3 = X.T @ dh3[r0:r1]
+        if on_dW is None:
+            dW1[i], dW3[i], dW2[i] = g1, g3, g2
+        else:
+            on_dW(e, g1, g3, g2)
     return dxd, dh1, dh3, dW1, dW3, dW2
 
 
@@ -317,12 +328,12 @@ def moe_forward(x, Wg, bias, W1, W3, W2, K, renorm=True, idx=None, logits=None,
                 tok_of=tok_of, xd=xd, h1=h1, h3=h3, a=a, y=y, out=out)
 
 
-def moe_backward(fw, dout, x, Wg, W1, W3, W2, K, renorm=True):
-    """The whole backward from a ``moe_forward`` record."""
+def moe_backward(fw, dout, x, Wg, W1, W3, W2, K, renorm=True, on_dW=None):
+    """The whole backward from a ``moe_forward`` record (``on_dW``: see expert_ffn_backward)."""
     dy, dg = combine_backward(dout, fw["y"], fw["row_of"], fw["gates"])
     dl = gate_backward(dg, fw["logits"], fw["idx"], renorm)
     dxd, dh1, dh3, dW1, dW3, dW2 = expert_ffn_backward(dy, fw["xd"], fw["cu"], W1, W3, W2,
-                                                       fw["h1"], fw["h3"], fw["a"])
+                                                       fw["h1"], fw["h3"], fw["a"], on_dW=on_dW)
     dx, dWg = dispatch_router_backward(dxd, fw["row_of"], dl, x, Wg, K)
     return dict(dy=dy, dg=dg, dlogits=dl, dxd=dxd, dh1=dh1, dh3=dh3, dW1=dW1, dW3=dW3,
                 dW2=dW2, dx=dx, dWg=dWg)
