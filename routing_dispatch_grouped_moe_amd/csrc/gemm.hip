@@ -8,30 +8,38 @@
 //   M-grouped  C[rows of e, N] = A[rows of e, K] * B_e[K, N]      (fwd, dA, dxd)
 //   K-grouped  C_e[M, N] = A[rows of e, M]^T * B[rows of e, N]    (dW1, dW3, dW2)
 //
-// gfx950 design.  A block computes a 128x128 tile (per B operand) with four
-// wavefronts as 2x2, each 64x64 on v_mfma_f32_32x32x16_bf16, fp32
-// accumulation.  Every operand tile is staged in LDS as rows of 64
-// K-contiguous bf16 (128 B) with the 16-byte chunk index XOR-ed by (row & 7),
-// so the MFMA fragment reads (8 rows x 16 B per quarter-wave) and the stage
-// writes are free of bank conflicts.  Operands stored K-contiguous in HBM are
-// copied chunk for chunk; operands stored with M or N contiguous (weights
-// [H, H'] in the forward, activations in the weight gradients) are read as
-// 8x8 bf16 blocks (eight 16-byte rows) and transposed in registers with
-// v_perm before the LDS write.  Global reads go through raw buffer
-// resources bounded to the expert's rows, so ragged tiles read zeros without
-// branches.  The next K step is prefetched into registers while the current
-// one runs on MFMA (two LDS stages, one barrier per step).  M tiles come
-// from a device-built table (expert, first row), so there is no host sync.
+// gfx950 design.  A block of eight wavefronts (2 x 4, two per SIMD)
+// computes a 256 x 256 tile (256 x (128 + 128) for the two-operand gate/up
+// and dW1/dW3 cases), each wavefront 128 x 64 as 4 x 2 (or 4 x 1 per
+// operand) v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators; the second
+// wavefront on a SIMD issues its LDS reads while the first one's MFMAs run.
+// K advances 64 per step.  Operand tiles live in LDS in one of two layouts,
+// both with a 16-byte-chunk XOR swizzle:
+//   - K-contiguous rows ([rows][64], 128 B a row) for operands stored
+//     K-major in HBM (activations in the forward, weights in dA/dxd);
+//     fragments are read with ds_read_b128;
+//   - K-major rows ([64][cols]) for operands stored with M or N contiguous
+//     (weights [H, H'] in the forward, activations in the weight gradients);
+//     fragments are read with the gfx950 LDS transpose load
+//     ds_read_b64_tr_b16, which hands each lane four consecutive-k values of
+//     one column, so no operand is ever transposed in registers.
+// Global reads are 16-byte buffer loads bounded to the expert's rows (reads
+// past the end return zero, which pads ragged M tiles and the ragged K tail
+// of the weight gradients).  The next K step is loaded into registers while
+// the current one runs on MFMA; LDS is double buffered with one barrier per
+// step.  M tiles come from a device-built table (expert, first row), so
+// nothing syncs with the host.
 //
 // The fp32 storage type (the tiny fp32 workload) uses a plain FMA kernel
-// with the same tile decomposition and epilogues.
+// with the same tile table and epilogues.
 #include "dev_common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kGroupM = 8;  // M tiles walked together (n fastest inside a group of 8 M tiles)
+constexpr int kBK = 64;
+constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
+constexpr int kGroupM = 4;  // M tiles walked together (n fastest inside the group)
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
 
@@ -85,17 +93,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 }
 
 // Tile coordinates of a block.  Returns false when the block has no tile.
-template <bool KGROUP, int BN>
+// valid: rows of the tile inside the expert (M-grouped) or the expert's row
+// count, i.e. the reduction length (K-grouped).
+template <bool KGROUP, int BM, int BN>
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int64_t& row0,
                                         int& valid, int& m0, int& n0) {
   if constexpr (KGROUP) {
     const int per_e = p.mtn * p.ntn;
     e = bid / per_e;
     const int rem = bid - e * per_e;
-    m0 = (rem / p.ntn) * kBM;
+    m0 = (rem / p.ntn) * BM;
     n0 = (rem % p.ntn) * BN;
     row0 = p.cu[e];
-    valid = max(0, p.cu[e + 1] - p.cu[e]);  // the reduction length
+    valid = max(0, p.cu[e + 1] - p.cu[e]);
     return true;
   } else {
     const int per_group = kGroupM * p.ntn;
@@ -106,131 +116,158 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
     const int2 t = p.tiles[mt];
     e = t.x;
     row0 = (int64_t)p.cu[e] + t.y;
-    valid = min(kBM, p.cu[e + 1] - (int)row0);
+    valid = min(BM, p.cu[e + 1] - (int)row0);
     m0 = 0;
     return true;
   }
 }
 
-// -------------------------------------------------------- LDS addressing --
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)row * 128u + ((uint32_t)(chunk ^ (row & 7)) << 4);
+// ------------------------------------------------------ LDS tile layouts --
+// K-contiguous tile [rows][64]: 128 B a row, chunk c (8 k values) stored at
+// c ^ (row & 7): the eight rows one ds_read_b128 quarter-wave touches hit
+// eight distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t kc_off(int row, int c) {
+  return (uint32_t)row * 128u + ((uint32_t)(c ^ (row & 7)) << 4);
+}
+// K-major tile [64][cols]: row k holds cols values, chunk c stored at
+// c ^ (2 * (k & 3)): the four rows x 32 bytes a 16-lane transpose-load group
+// reads hit eight distinct 16-byte bank groups.
+template <int COLS>
+__device__ __forceinline__ uint32_t km_off(int k, int c) {
+  return (uint32_t)k * (COLS * 2) + ((uint32_t)(c ^ (2 * (k & 3))) << 4);
 }
 
-// 8x8 bf16 transpose: in[j] holds 8 consecutive-MN values at k = j; out[m]
-// holds the 8 k values (k pairs packed per dword) of MN index m.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      out[m][q] = __builtin_amdgcn_perm(in[2 * q + 1][m >> 1], in[2 * q][m >> 1],
-                                        (m & 1) ? 0x07060302u : 0x05040100u);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
 }
 
-// One operand tile of ROWS x 64 (rows = M or N index, 64 = K step) staged via
-// registers.  KC: stored [rows][K] in HBM (K contiguous); otherwise [K][rows].
+// MFMA 32x32x16 operand fragment (8 k values of one M/N index per lane, lane
+// l: index l % 32, k = 8 (l / 32) + 0..7) from a K-contiguous tile.
+__device__ __forceinline__ u32x4 frag_kc(const char* tile, int row_base, int kk, int lane) {
+  const int row = row_base + (lane & 31);
+  return lds_read16(tile, kc_off(row, 2 * kk + (lane >> 5)));
+}
+// The same fragment from a K-major tile, with two transpose loads: in each
+// 16-lane group, lane s reads four values of row k0 + s/4 at column
+// 4*(s%4); lane i then holds column i of rows k0..k0+3.
+template <int COLS>
+__device__ __forceinline__ u32x4 frag_km(const char* tile, int col_base, int kk, int lane) {
+  const int col = col_base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int kb = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = kb + 4 * h;
+    const uint32_t off = km_off<COLS>(k, col >> 3) + (col & 7) * 2;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)((__attribute__((address_space(3))) char*)(tile) + off));
+    const u32x2 u = __builtin_bit_cast(u32x2, v);
+    r[2 * h] = u[0];
+    r[2 * h + 1] = u[1];
+  }
+  return r;
+}
+
+// One operand tile of one K step, staged global -> registers -> LDS.
+//   KC:  stored [rows][K] in HBM, tile rows [0, ROWS), k [k0, k0+64)
+//   !KC: stored [K][cols] in HBM, tile k rows [k0, k0+64), cols [c0, c0+ROWS)
 template <bool KC, int ROWS, int NOPS>
-struct OperandStage {
-  static constexpr int kItems = NOPS * (KC ? ROWS * 8 : ROWS);  // 16-B chunks or 8x8 blocks
-  static constexpr int kSlots = (kItems + 255) / 256;
-  static constexpr int kRegs = KC ? kSlots : kSlots * 8;
-  u32x4 r[kRegs];
+struct Stager {
+  static constexpr int kChunks = ROWS * (kBK / 8);          // 16-byte chunks per operand
+  static constexpr int kPer = NOPS * kChunks / kThreads;    // per thread
+  static_assert(NOPS * kChunks % kThreads == 0, "tile not a multiple of the block");
+  u32x4 r[kPer];
 
-  // rs[op]: resource of operand op; off0: byte offset of (row 0 or k 0) of this K step.
-  // For KC, element (row, k) is at (row*ld + k); otherwise at (k*ld + row).
   __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t (&rs)[NOPS], int64_t ld,
-                                       int row_base, int k0, int tid) {
+                                       int base, int k0, int tid) {
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      const int it = tid + 256 * sl;
-      if (it >= kItems) break;
-      const int op = NOPS == 1 ? 0 : it / (kItems / NOPS);
-      const int li = NOPS == 1 ? it : it - op * (kItems / NOPS);
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + kThreads * i;
+      const int op = q / kChunks, lq = q % kChunks;
+      int64_t el;
       if constexpr (KC) {
-        const int row = li >> 3, c = li & 7;
-        r[sl] = buf_load16(rs[op], (uint32_t)(((int64_t)(row_base + row) * ld + k0 + c * 8) * 2));
+        el = (int64_t)(base + (lq >> 3)) * ld + k0 + (lq & 7) * 8;
       } else {
-        const int kg = li & 7, mg = li >> 3;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          r[sl * 8 + j] = buf_load16(
-              rs[op], (uint32_t)(((int64_t)(k0 + kg * 8 + j) * ld + row_base + mg * 8) * 2));
+        constexpr int cpr = ROWS / 8;  // chunks per k row
+        el = (int64_t)(k0 + lq / cpr) * ld + base + (lq % cpr) * 8;
       }
+      r[i] = buf_load16(rs[op], (uint32_t)(el * 2));
     }
   }
-  __device__ __forceinline__ void store(char* lds, int tid) {
+  __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      const int it = tid + 256 * sl;
-      if (it >= kItems) break;
-      const int op = NOPS == 1 ? 0 : it / (kItems / NOPS);
-      const int li = NOPS == 1 ? it : it - op * (kItems / NOPS);
-      char* t = lds + op * (ROWS * 128);
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + kThreads * i;
+      const int op = q / kChunks, lq = q % kChunks;
+      char* t = lds + op * (ROWS * kBK * 2);
+      uint32_t off;
       if constexpr (KC) {
-        const int row = li >> 3, c = li & 7;
-        *reinterpret_cast<u32x4*>(t + lds_off(row, c)) = r[sl];
+        off = kc_off(lq >> 3, lq & 7);
       } else {
-        const int kg = li & 7, mg = li >> 3;
-        u32x4 in[8], out[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) in[j] = r[sl * 8 + j];
-        transpose8x8(in, out);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) *reinterpret_cast<u32x4*>(t + lds_off(mg * 8 + m, kg)) = out[m];
+        constexpr int cpr = ROWS / 8;
+        off = km_off<ROWS>(lq / cpr, lq % cpr);
       }
+      *reinterpret_cast<u32x4*>(t + off) = r[i];
     }
   }
 };
 
-template <bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
+// Wait for this wave's LDS accesses, then a workgroup barrier.  Global loads
+// stay in flight (no vmcnt wait) and the compiler may not move memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int kTileA = kBM * 128, kTileB = kBN * 128;  // bytes per stage
+  constexpr int WM = BM / 2, WN = BN / 4;      // wavefront tile (per B operand)
+  constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
+  constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
   int64_t row0;
-  if (!tile_of<KGROUP, kBN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
 
-  // Resources and tile origins.
   __amdgpu_buffer_rsrc_t ra[TWOSEG ? 2 : 1];
-  __amdgpu_buffer_rsrc_t rb[TWOSEG ? 2 : NB];
-  int a_base, b_base;  // row (KC) or column (not KC) origin inside the resource
-  int nk;
+  __amdgpu_buffer_rsrc_t rb[(DUAL || TWOSEG) ? 2 : 1];
+  int a_base, b_base, nk;
   const int nk_seg = KGROUP ? 0 : p.K / kBK;
   if constexpr (KGROUP) {
-    // A: [rows][M] of expert e; B: [rows][N]; reduction over the expert's rows.
+    // A: [rows][M] of expert e (A^T read), B: [rows][N]; the reduction runs over the rows.
     if (valid == 0) {
       if (!p.accum) {
-        for (int i = tid; i < kBM * kBN; i += 256) {
-          const int r = i / kBN, c = i % kBN;
-          epilogue<EPI, true, DUAL>(p, e, m0 + r, n0 + c, 0.f, 0.f);
+        for (int i = tid; i < BM * BN; i += kThreads) {
+          const int r = i / BN, c = i % BN;
+          if (m0 + r < p.M && n0 + c < p.N) epilogue<EPI, true, DUAL>(p, e, m0 + r, n0 + c, 0.f, 0.f);
         }
       }
       return;
     }
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
-    ra[0] = make_rsrc(A, (uint32_t)((int64_t)valid * p.lda * 2));
-    const uint16_t* B0 = reinterpret_cast<const uint16_t*>(p.B0) + row0 * p.ldb;
-    rb[0] = make_rsrc(B0, (uint32_t)((int64_t)valid * p.ldb * 2));
-    if constexpr (DUAL) {
-      const uint16_t* B1 = reinterpret_cast<const uint16_t*>(p.B1) + row0 * p.ldb;
-      rb[1] = make_rsrc(B1, (uint32_t)((int64_t)valid * p.ldb * 2));
-    }
+    ra[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda,
+                      (uint32_t)((int64_t)valid * p.lda * 2));
+    rb[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B0) + row0 * p.ldb,
+                      (uint32_t)((int64_t)valid * p.ldb * 2));
+    if constexpr (DUAL)
+      rb[1] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B1) + row0 * p.ldb,
+                        (uint32_t)((int64_t)valid * p.ldb * 2));
     a_base = m0;
     b_base = n0;
     nk = (valid + kBK - 1) / kBK;
   } else {
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
-    ra[0] = make_rsrc(A, (uint32_t)((int64_t)valid * p.lda * 2));
-    if constexpr (TWOSEG) {
-      const uint16_t* A1 = reinterpret_cast<const uint16_t*>(p.A1) + row0 * p.lda;
-      ra[1] = make_rsrc(A1, (uint32_t)((int64_t)valid * p.lda * 2));
-    }
+    ra[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda,
+                      (uint32_t)((int64_t)valid * p.lda * 2));
+    if constexpr (TWOSEG)
+      ra[1] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A1) + row0 * p.lda,
+                        (uint32_t)((int64_t)valid * p.lda * 2));
     const uint32_t wbytes = (uint32_t)((int64_t)p.N * p.K * 2);
     rb[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B0) + (int64_t)e * p.sBe, wbytes);
     if constexpr (DUAL || TWOSEG)
@@ -240,110 +277,130 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
     nk = TWOSEG ? 2 * nk_seg : nk_seg;
   }
 
-  OperandStage<A_KC, kBM, 1> sa;
-  OperandStage<B_KC, kBN, NB> sb;
-  auto load_step = [&](int kt) {
+  Stager<A_KC, BM, 1> sa;
+  Stager<B_KC, BN, NB> sb;
+  auto load = [&](int kt) {
     int seg = 0, k0 = kt * kBK;
     if constexpr (TWOSEG) {
       seg = kt >= nk_seg ? 1 : 0;
       k0 = (kt - seg * nk_seg) * kBK;
-    }
-    __amdgpu_buffer_rsrc_t rA[1] = {ra[TWOSEG ? seg : 0]};
-    sa.load(rA, p.lda, a_base, k0, tid);
-    if constexpr (TWOSEG) {
-      __amdgpu_buffer_rsrc_t rB[1] = {rb[seg]};
+      const __amdgpu_buffer_rsrc_t rA[1] = {seg ? ra[1] : ra[0]};
+      const __amdgpu_buffer_rsrc_t rB[1] = {seg ? rb[1] : rb[0]};
+      sa.load(rA, p.lda, a_base, k0, tid);
       sb.load(rB, p.ldb, b_base, k0, tid);
     } else {
-      sb.load(rb, p.ldb, b_base, k0, tid);
+      sa.load(ra, p.lda, a_base, k0, tid);
+      if constexpr (DUAL) {
+        sb.load(rb, p.ldb, b_base, k0, tid);
+      } else {
+        const __amdgpu_buffer_rsrc_t rB[1] = {rb[0]};
+        sb.load(rB, p.ldb, b_base, k0, tid);
+      }
     }
   };
 
-  f32x16 acc[NB][2][2];
+  f32x16 acc[NB][MI][NJ];
 #pragma unroll
   for (int q = 0; q < NB; ++q)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[q][i][j][v] = 0.f;
 
-  load_step(0);
-  sa.store(smem, tid);
-  sb.store(smem + kTileA, tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStage;
-    if (kt + 1 < nk) load_step(kt + 1);
+  auto compute = [&](const char* st) {
+    const char* tA = st;
+    const char* tB = st + kTileA;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = kk * 2 + (lane >> 5);
-      u32x4 af[2], bfr[NB][2];
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      u32x4 af[MI], bfr[NB][NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(cur + lds_off(wm * 64 + i * 32 + (lane & 31), chunk));
+      for (int i = 0; i < MI; ++i) {
+        if constexpr (A_KC) af[i] = frag_kc(tA, wm * WM + i * 32, kk, lane);
+        else af[i] = frag_km<BM>(tA, wm * WM + i * 32, kk, lane);
+      }
 #pragma unroll
       for (int q = 0; q < NB; ++q)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[q][j] = *reinterpret_cast<const u32x4*>(cur + kTileA + q * kTileB +
-                                                      lds_off(wn * 64 + j * 32 + (lane & 31), chunk));
+        for (int j = 0; j < NJ; ++j) {
+          const char* t = tB + q * kTileB;
+          if constexpr (B_KC) bfr[q][j] = frag_kc(t, wn * WN + j * 32, kk, lane);
+          else bfr[q][j] = frag_km<BN>(t, wn * WN + j * 32, kk, lane);
+        }
 #pragma unroll
-      for (int q = 0; q < NB; ++q)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < NB; ++q)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[q][j]),
                 acc[q][i][j], 0, 0, 0);
+      // keep one K16 slice of fragments live at a time (register budget of
+      // two wavefronts per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  load(0);
+  sa.store(smem, tid);
+  sb.store(smem + kTileA, tid);
+  lds_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * kStage;
+    char* nxt = smem + ((kt + 1) & 1) * kStage;
+    if (kt + 1 < nk) load(kt + 1);
+    compute(cur);
     if (kt + 1 < nk) {
-      char* nxt = smem + ((kt + 1) & 1) * kStage;
       sa.store(nxt, tid);
       sb.store(nxt + kTileA, tid);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // 32x32 MFMA result: lane holds column (lane % 32), rows 8*(v/4) + 4*(lane/32) + v%4.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j) {
+      const int c = n0 + wn * WN + j * 32 + (lane & 31);
+      if (c >= p.N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int c = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
         if constexpr (KGROUP) {
-          epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
+          if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
         } else {
           if (r < valid) epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v], v1);
         }
       }
+    }
 }
 
 // ---------------------------------------------------------- fp32 kernel --
-// Tile 128 (M) x 32 (N); thread (tid % 32) owns a column, rows tid/32 + 8 i.
-constexpr int kBNf = 32;
+// M tile of kGemmBM rows x 32 columns; thread (tid % 32) owns a column,
+// rows tid/32 + 8 i.
+constexpr int kBMf = kGemmBM, kBNf = 32;
 
 template <bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   int e, valid, m0, n0;
   int64_t row0;
-  if (!tile_of<KGROUP, kBNf>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  if (!tile_of<KGROUP, kBMf, kBNf>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
   const int tid = threadIdx.x;
   const int col = n0 + (tid & 31);
+  if (col >= p.N) return;
   const float* A0 = reinterpret_cast<const float*>(p.A0);
   const float* A1 = reinterpret_cast<const float*>(p.A1);
   const float* B0 = reinterpret_cast<const float*>(p.B0);
   const float* B1 = reinterpret_cast<const float*>(p.B1);
-  for (int i = 0; i < kBM / 8; ++i) {
+  for (int i = 0; i < kBMf / 8; ++i) {
     const int r = (tid >> 5) + 8 * i;
     float acc0 = 0.f, acc1 = 0.f;
     if constexpr (KGROUP) {
+      if (m0 + r >= p.M) continue;
       // C_e[m0+r, col] = sum over the expert's rows k of A[k, m0+r] * B[k, col]
       for (int k = 0; k < valid; ++k) {
         const int64_t gr = row0 + k;
@@ -396,10 +453,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   // A malformed cu (not monotone) yields no tiles for that expert rather than
   // a table overflow.
   const int c = e < E ? max(0, cu[e + 1] - cu[e]) : 0;
-  const int nt = (c + kBM - 1) / kBM;
+  const int nt = (c + kGemmBM - 1) / kGemmBM;
   int total;
   const int start = block_exclusive_scan_1024_g(nt, sh, &total);
-  for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * kBM);
+  for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * kGemmBM);
   if (e == 0) *ntiles = min(total, max_tiles);
 }
 
@@ -410,13 +467,14 @@ void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hi
 }
 
 // -------------------------------------------------------------- launches --
-template <bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
+template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
-  const int bn = bf16 ? kBN : kBNf;
-  p.ntn = p.N / bn;
+  static_assert(KGROUP || BM == kGemmBM, "M-grouped tiles follow the tile table");
+  const int bm = bf16 ? BM : kBMf, bn = bf16 ? BN : kBNf;
+  p.ntn = (p.N + bn - 1) / bn;
   int blocks;
   if (KGROUP) {
-    p.mtn = p.M / kBM;
+    p.mtn = (p.M + bm - 1) / bm;
     blocks = p.E * p.mtn * p.ntn;
   } else {
     const int groups = (max_mtiles + kGroupM - 1) / kGroupM;
@@ -425,15 +483,15 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   if (blocks <= 0) return;
   TimedLaunch tl(name, s);
   if (bf16) {
-    auto kern = gemm_bf16_kernel<A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
-    constexpr int lds = 2 * (kBM * 128 + (DUAL ? 2 : 1) * kBN * 128);
+    auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
+    constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
     if (!attr) {
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       attr = true;
     }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, s, p);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, p);
   } else {
     hipLaunchKernelGGL((gemm_f32_kernel<A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>), dim3(blocks),
                        dim3(256), 0, s, p);
@@ -453,23 +511,27 @@ void launch_ffn_up(const void* xd, const int32_t* cu, const void* W1, const void
                    void* h3, void* a, int64_t R, int H, int Hf, int E, const WsLayout& L, char* ws,
                    bool bf16, hipStream_t s) {
   (void)R;
+  // [h1 | h3][rows, Hf] = xd[rows, H] * [W1[e] | W3[e]]; W is [H][Hf] = [K][N].
   GemmArgs p = base_args(cu, L, ws, E);
   p.N = Hf; p.K = H;
   p.A0 = xd; p.lda = H;
   p.B0 = W1; p.B1 = W3; p.ldb = Hf; p.sBe = (int64_t)H * Hf;
   p.C0 = h1; p.C1 = h3; p.C2 = a; p.ldc = Hf;
-  gemm_launch<true, false, true, false, false, EPI_SWIGLU_FWD>("ffn_up", p, L.max_tiles, bf16, s);
+  gemm_launch<256, 128, true, false, true, false, false, EPI_SWIGLU_FWD>("ffn_up", p, L.max_tiles,
+                                                                         bf16, s);
 }
 
 void launch_ffn_down(const void* a, const int32_t* cu, const void* W2, void* y, int64_t R, int H,
                      int Hf, int E, const WsLayout& L, char* ws, bool bf16, hipStream_t s) {
   (void)R;
+  // y[rows, H] = a[rows, Hf] * W2[e]; W2[e] is [Hf][H] = [K][N].
   GemmArgs p = base_args(cu, L, ws, E);
   p.N = H; p.K = Hf;
   p.A0 = a; p.lda = Hf;
   p.B0 = W2; p.ldb = H; p.sBe = (int64_t)Hf * H;
   p.C0 = y; p.ldc = H;
-  gemm_launch<true, false, false, false, false, EPI_STORE>("ffn_down", p, L.max_tiles, bf16, s);
+  gemm_launch<256, 256, true, false, false, false, false, EPI_STORE>("ffn_down", p, L.max_tiles,
+                                                                     bf16, s);
 }
 
 void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void* h1,
@@ -483,7 +545,8 @@ void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void
   p.B0 = W2; p.ldb = H; p.sBe = (int64_t)Hf * H;
   p.C0 = dh1; p.C1 = dh3; p.ldc = Hf;
   p.X0 = h1; p.X1 = h3;
-  gemm_launch<true, true, false, false, false, EPI_SWIGLU_BWD>("bwd_dA", p, L.max_tiles, bf16, s);
+  gemm_launch<256, 256, true, true, false, false, false, EPI_SWIGLU_BWD>("bwd_dA", p, L.max_tiles,
+                                                                         bf16, s);
 }
 
 void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const void* W1,
@@ -496,7 +559,8 @@ void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const v
   p.A0 = dh1; p.A1 = dh3; p.lda = Hf;
   p.B0 = W1; p.B1 = W3; p.ldb = Hf; p.sBe = (int64_t)H * Hf;
   p.C0 = dxd; p.ldc = H;
-  gemm_launch<true, true, false, true, false, EPI_STORE>("bwd_dxd", p, L.max_tiles, bf16, s);
+  gemm_launch<256, 256, true, true, false, true, false, EPI_STORE>("bwd_dxd", p, L.max_tiles, bf16,
+                                                                   s);
 }
 
 void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,
@@ -509,7 +573,7 @@ void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2
   p.B0 = dy; p.ldb = H;
   p.C0 = dW2; p.ldc = H; p.sCe = (int64_t)Hf * H;
   p.accum = accum;
-  gemm_launch<false, false, false, false, true, EPI_F32>("bwd_dW2", p, 0, bf16, s);
+  gemm_launch<256, 256, false, false, false, false, true, EPI_F32>("bwd_dW2", p, 0, bf16, s);
 }
 
 void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int32_t* cu,
@@ -523,7 +587,7 @@ void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int
   p.B0 = dh1; p.B1 = dh3; p.ldb = Hf;
   p.C0 = dW1; p.C1 = dW3; p.ldc = Hf; p.sCe = (int64_t)H * Hf;
   p.accum = accum;
-  gemm_launch<false, false, true, false, true, EPI_F32>("bwd_dW13", p, 0, bf16, s);
+  gemm_launch<256, 128, false, false, true, false, true, EPI_F32>("bwd_dW13", p, 0, bf16, s);
 }
 
 }  // namespace moe

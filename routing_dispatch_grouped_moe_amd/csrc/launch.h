@@ -37,7 +37,7 @@ struct WsLayout {
 };
 WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
 
-constexpr int kGemmBM = 128;  // M tile of the grouped GEMMs (rows per tile)
+constexpr int kGemmBM = 256;  // M tile of the grouped GEMMs (rows per tile)
 
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
