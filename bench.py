@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 512 MiB device-to-device copy first (a known-size kernel for "
+                         "scaling HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU expert-"
@@ -187,6 +190,14 @@ def main():
     def say(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # one elementwise kernel: 512 MiB read, 512 MiB written
+        torch.cuda.synchronize()
+        say("calibration kernel (neg): 512 MiB read + 512 MiB written")
+        del src, dst
     say(f"{cfg['workload']}: inputs resident; warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
