@@ -11,10 +11,12 @@
 // gfx950 design.  A block of eight wavefronts (2 x 4, two per SIMD)
 // computes a 256 x 256 tile (256 x (128 + 128) for the two-operand gate/up
 // and dW1/dW3 cases), each wavefront 128 x 64 as 4 x 2 (or 4 x 1 per
-// operand) v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators; the second
-// wavefront on a SIMD issues its LDS reads while the first one's MFMAs run.
-// K advances 64 per step.  Operand tiles live in LDS in one of two layouts,
-// both with a 16-byte-chunk XOR swizzle:
+// operand) v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators; with two
+// wavefronts per SIMD one issues MFMAs while the other waits on LDS.  K
+// advances 64 per step.  Operand tiles live in LDS in one of two layouts,
+// both XOR-swizzled on 16-byte chunks for the 64-bank LDS (a ds_read_b128
+// serves 16 lanes per cycle; measured conflict-free with a bank-conflict
+// probe):
 //   - K-contiguous rows ([rows][64], 128 B a row) for operands stored
 //     K-major in HBM (activations in the forward, weights in dA/dxd);
 //     fragments are read with ds_read_b128;
@@ -28,7 +30,8 @@
 // of the weight gradients).  The next K step is loaded into registers while
 // the current one runs on MFMA; LDS is double buffered with one barrier per
 // step.  M tiles come from a device-built table (expert, first row), so
-// nothing syncs with the host.
+// nothing syncs with the host; their block ids are renumbered so that each
+// XCD (own L2) runs a contiguous patch of tiles.
 //
 // The fp32 storage type (the tiny fp32 workload) uses a plain FMA kernel
 // with the same tile table and epilogues.
@@ -37,8 +40,7 @@
 
 namespace moe {
 
-constexpr int kBK = 64;      // K per step
-constexpr int kStages = 2;  // LDS ring depth (kStages - 1 steps of loads in flight)
+constexpr int kBK = 64;
 constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
 constexpr int kGroupM = 4;  // M tiles walked together (n fastest inside the group)
 
@@ -139,36 +141,24 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
 }
 
 // ------------------------------------------------------ LDS tile layouts --
-// LDS on gfx950 has 64 four-byte banks: a ds_read_b128 serves 16 lanes
-// (256 B) per cycle.  Operand tiles are filled by buffer_load ... lds (each
-// wave instruction writes 1 KB, lane l at +16 l), so the layouts below are
-// produced by choosing which global chunk every lane fetches.
-//
-// K-contiguous tile [rows][kBK]: chunk c (8 k values) of a row stored at
-// c ^ swz(row), chosen so that the sixteen rows (same chunk) one read cycle
-// touches land on sixteen distinct 16-byte bank groups.
-constexpr int kRowBytes = kBK * 2;
-__device__ __forceinline__ int kc_swz(int row) {
-  return kBK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
+// K-contiguous tile [rows][64]: 128 B a row, chunk c (8 k values) stored at
+// c ^ ((row >> 1) & 7): the sixteen rows (same chunk) one read cycle touches
+// land on sixteen distinct 16-byte bank groups.
 __device__ __forceinline__ uint32_t kc_off(int row, int c) {
-  return (uint32_t)row * kRowBytes + ((uint32_t)(c ^ kc_swz(row)) << 4);
+  return (uint32_t)row * 128u + ((uint32_t)(c ^ ((row >> 1) & 7)) << 4);
 }
-__device__ __forceinline__ int kc_logical(int row, int phys) { return phys ^ kc_swz(row); }
-// K-major tile [kBK][cols]: row k holds cols values, chunk c stored at
+// K-major tile [64][cols]: row k holds cols values, chunk c stored at
 // c ^ (4 (k & 3) ^ 2 ((k >> 3) & 1)): the 4 rows x 64 B that 32 lanes of a
 // transpose load read (k0..k0+3, four aligned chunks) cover all sixteen
 // 16-byte bank groups, and rows k and k+8 (the other half of the wave) are
 // shifted against each other.
-__device__ __forceinline__ int km_swz(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 template <int COLS>
 __device__ __forceinline__ uint32_t km_off(int k, int c) {
-  return (uint32_t)k * (COLS * 2) + ((uint32_t)(c ^ km_swz(k)) << 4);
+  return (uint32_t)k * (COLS * 2) + ((uint32_t)(c ^ (4 * (k & 3)) ^ (2 * ((k >> 3) & 1))) << 4);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(base + off);
@@ -201,88 +191,76 @@ __device__ __forceinline__ u32x4 frag_km(const char* tile, int col_base, int kk,
   return r;
 }
 
-// Direct global -> LDS staging of one operand (NOPS tiles of ROWS x kBK).
-// Each wavefront issues kPer 1-KB buffer_load ... lds per K step; the lane's
-// voffset for K step 0 is precomputed, later steps add k0 (KC) or k0 rows.
-//   KC:  stored [rows][K] in HBM: LDS tile [ROWS][kBK]
-//   !KC: stored [K][cols] in HBM: LDS tile [kBK][ROWS]
+// One operand tile of one K step, staged global -> registers -> LDS.
+//   KC:  stored [rows][K] in HBM, tile rows [0, ROWS), k [k0, k0+64)
+//   !KC: stored [K][cols] in HBM, tile k rows [k0, k0+64), cols [c0, c0+ROWS)
 template <bool KC, int ROWS, int NOPS>
-struct DmaOperand {
-  static constexpr int kInstr = NOPS * ROWS * kRowBytes / 1024;  // 1-KB wave instructions per step
-  static constexpr int kPer = kInstr / 8;                  // per wavefront (eight wavefronts)
-  static_assert(kInstr % 8 == 0, "operand tile not a multiple of 8 KB");
-  uint32_t voff[kPer];                                     // byte offset of K step 0
+struct Stager {
+  static constexpr int kChunks = ROWS * (kBK / 8);          // 16-byte chunks per operand
+  static constexpr int kPer = NOPS * kChunks / kThreads;    // per thread
+  static_assert(NOPS * kChunks % kThreads == 0, "tile not a multiple of the block");
+  u32x4 r[kPer];
 
-  __device__ __forceinline__ void init(int64_t ld, int base, int w, int lane) {
+  __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t (&rs)[NOPS], int64_t ld,
+                                       int base, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ins = w * kPer + i;                        // wave instruction id
-      const int op = ins / (kInstr / NOPS);
-      const int P = (ins - op * (kInstr / NOPS)) * 64 + lane;  // physical 16-B chunk in the tile
+      const int q = tid + kThreads * i;
+      const int op = q / kChunks, lq = q % kChunks;
       int64_t el;
       if constexpr (KC) {
-        constexpr int cpr = kBK / 8;  // chunks per row
-        const int row = P / cpr;
-        el = (int64_t)(base + row) * ld + kc_logical(row, P % cpr) * 8;
+        el = (int64_t)(base + (lq >> 3)) * ld + k0 + (lq & 7) * 8;
       } else {
-        constexpr int cpr = ROWS / 8;
-        const int k = P / cpr;
-        el = (int64_t)k * ld + base + ((P % cpr) ^ km_swz(k)) * 8;
+        constexpr int cpr = ROWS / 8;  // chunks per k row
+        el = (int64_t)(k0 + lq / cpr) * ld + base + (lq % cpr) * 8;
       }
-      voff[i] = (uint32_t)(el * 2);
+      r[i] = buf_load16(rs[op], (uint32_t)(el * 2));
     }
   }
-  // Issue this wavefront's loads of K step k0 into tile memory `lds`.  The
-  // step's offset moves the resource base (scalar work) rather than the
-  // per-lane offsets, so the lane offsets stay loop invariant and every read
-  // is still range checked against the operand's end.
-  __device__ __forceinline__ void issue(const uint16_t* const (&base)[NOPS], uint32_t bytes,
-                                        char* lds, int64_t ld, int k0, int w) const {
-    const uint32_t kadd = KC ? (uint32_t)k0 * 2u : (uint32_t)((int64_t)k0 * ld * 2);
-    // (forced into an SGPR: the compiler lowers this saturating subtract on
-    // the vector unit, and a descriptor word in a VGPR would force a
-    // per-lane loop around every load)
-    const uint32_t left = __builtin_amdgcn_readfirstlane(bytes - min(kadd, bytes));
+  __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ins = w * kPer + i;
-      const int op = ins / (kInstr / NOPS);
-      char* dst = lds + ins * 1024;
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(reinterpret_cast<const char*>(base[op]) + kadd, left);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff[i], 0, 0, 0);
+      const int q = tid + kThreads * i;
+      const int op = q / kChunks, lq = q % kChunks;
+      char* t = lds + op * (ROWS * kBK * 2);
+      uint32_t off;
+      if constexpr (KC) {
+        off = kc_off(lq >> 3, lq & 7);
+      } else {
+        constexpr int cpr = ROWS / 8;
+        off = km_off<ROWS>(lq / cpr, lq % cpr);
+      }
+      *reinterpret_cast<u32x4*>(t + off) = r[i];
     }
   }
 };
 
+// Wait for this wave's LDS accesses, then a workgroup barrier.  Global loads
+// stay in flight (no vmcnt wait) and the compiler may not move memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int WM = BM / 2, WN = BN / 4;      // wavefront tile (per B operand)
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
-  static_assert(kStage * kStages <= 160 * 1024, "LDS ring too large");
-  // Ring of four K-step stages: three steps of loads in flight while one is
-  // computed.  Completion of a stage's loads is awaited explicitly (vmcnt)
-  // before the barrier that publishes it.
-  extern __shared__ __attribute__((aligned(1024))) char stg[];  // kStages * kStage bytes
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
   int64_t row0;
   if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
 
-  const uint16_t* pa[TWOSEG ? 2 : 1];
-  const uint16_t* pb[(DUAL || TWOSEG) ? 2 : 1];
-  uint32_t abytes, bbytes;
-  int nk;
+  __amdgpu_buffer_rsrc_t ra[TWOSEG ? 2 : 1];
+  __amdgpu_buffer_rsrc_t rb[(DUAL || TWOSEG) ? 2 : 1];
+  int a_base, b_base, nk;
   const int nk_seg = KGROUP ? 0 : p.K / kBK;
-  DmaOperand<A_KC, BM, 1> da;
-  DmaOperand<B_KC, BN, NB> db;
   if constexpr (KGROUP) {
     // A: [rows][M] of expert e (A^T read), B: [rows][N]; the reduction runs over the rows.
     if (valid == 0) {
@@ -294,43 +272,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       }
       return;
     }
-    pa[0] = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
-    pb[0] = reinterpret_cast<const uint16_t*>(p.B0) + row0 * p.ldb;
-    if constexpr (DUAL) pb[1] = reinterpret_cast<const uint16_t*>(p.B1) + row0 * p.ldb;
-    abytes = (uint32_t)((int64_t)valid * p.lda * 2);
-    bbytes = (uint32_t)((int64_t)valid * p.ldb * 2);
-    da.init(p.lda, m0, w, lane);
-    db.init(p.ldb, n0, w, lane);
+    ra[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda,
+                      (uint32_t)((int64_t)valid * p.lda * 2));
+    rb[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B0) + row0 * p.ldb,
+                      (uint32_t)((int64_t)valid * p.ldb * 2));
+    if constexpr (DUAL)
+      rb[1] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B1) + row0 * p.ldb,
+                        (uint32_t)((int64_t)valid * p.ldb * 2));
+    a_base = m0;
+    b_base = n0;
     nk = (valid + kBK - 1) / kBK;
   } else {
-    pa[0] = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
-    if constexpr (TWOSEG) pa[1] = reinterpret_cast<const uint16_t*>(p.A1) + row0 * p.lda;
-    abytes = (uint32_t)((int64_t)valid * p.lda * 2);
-    pb[0] = reinterpret_cast<const uint16_t*>(p.B0) + (int64_t)e * p.sBe;
-    if constexpr (DUAL || TWOSEG) pb[1] = reinterpret_cast<const uint16_t*>(p.B1) + (int64_t)e * p.sBe;
-    bbytes = (uint32_t)((int64_t)p.N * p.K * 2);
-    da.init(p.lda, 0, w, lane);
-    db.init(p.ldb, n0, w, lane);
+    ra[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda,
+                      (uint32_t)((int64_t)valid * p.lda * 2));
+    if constexpr (TWOSEG)
+      ra[1] = make_rsrc(reinterpret_cast<const uint16_t*>(p.A1) + row0 * p.lda,
+                        (uint32_t)((int64_t)valid * p.lda * 2));
+    const uint32_t wbytes = (uint32_t)((int64_t)p.N * p.K * 2);
+    rb[0] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B0) + (int64_t)e * p.sBe, wbytes);
+    if constexpr (DUAL || TWOSEG)
+      rb[1] = make_rsrc(reinterpret_cast<const uint16_t*>(p.B1) + (int64_t)e * p.sBe, wbytes);
+    a_base = 0;
+    b_base = n0;
     nk = TWOSEG ? 2 * nk_seg : nk_seg;
   }
 
-  // Issue the loads of K step kt into stage memory st.
-  auto issue = [&](char* st, int kt) {
+  Stager<A_KC, BM, 1> sa;
+  Stager<B_KC, BN, NB> sb;
+  auto load = [&](int kt) {
+    int seg = 0, k0 = kt * kBK;
     if constexpr (TWOSEG) {
-      const int seg = kt >= nk_seg ? 1 : 0;
-      const int k0 = (kt - seg * nk_seg) * kBK;
-      const uint16_t* const bA[1] = {seg ? pa[1] : pa[0]};
-      const uint16_t* const bB[1] = {seg ? pb[1] : pb[0]};
-      da.issue(bA, abytes, st, p.lda, k0, w);
-      db.issue(bB, bbytes, st + kTileA, p.ldb, k0, w);
+      seg = kt >= nk_seg ? 1 : 0;
+      k0 = (kt - seg * nk_seg) * kBK;
+      const __amdgpu_buffer_rsrc_t rA[1] = {seg ? ra[1] : ra[0]};
+      const __amdgpu_buffer_rsrc_t rB[1] = {seg ? rb[1] : rb[0]};
+      sa.load(rA, p.lda, a_base, k0, tid);
+      sb.load(rB, p.ldb, b_base, k0, tid);
     } else {
-      const int k0 = kt * kBK;
-      da.issue(pa, abytes, st, p.lda, k0, w);
+      sa.load(ra, p.lda, a_base, k0, tid);
       if constexpr (DUAL) {
-        db.issue(pb, bbytes, st + kTileA, p.ldb, k0, w);
+        sb.load(rb, p.ldb, b_base, k0, tid);
       } else {
-        const uint16_t* const bB[1] = {pb[0]};
-        db.issue(bB, bbytes, st + kTileA, p.ldb, k0, w);
+        const __amdgpu_buffer_rsrc_t rB[1] = {rb[0]};
+        sb.load(rB, p.ldb, b_base, k0, tid);
       }
     }
   };
@@ -373,58 +357,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
             acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[q][j]),
                 acc[q][i][j], 0, 0, 0);
+      // keep one K16 slice of fragments live at a time (register budget of
+      // two wavefronts per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // K-grouped tail: rows past the expert's end must read as zero.  Loads
-  // past the resource end are not relied on to write the LDS; the rows are
-  // cleared here once the step's loads have landed.
-  const int tail = KGROUP ? (valid & (kBK - 1)) : 0;
-  auto clear_tail = [&](char* st) {
-    constexpr int kRowA = BM * 2, kRowB = BN * 2;  // bytes of one k row (K-major tiles)
-    for (int i = tid; i < (kBK - tail) * (kRowA + NB * kRowB) / 16; i += kThreads) {
-      const int per = (kRowA + NB * kRowB) / 16;
-      const int k = tail + i / per, c = i % per;
-      char* dst;
-      if (c < kRowA / 16) dst = st + k * kRowA + c * 16;
-      else {
-        const int cb = c - kRowA / 16, q = cb / (kRowB / 16);
-        dst = st + kTileA + q * kTileB + k * kRowB + (cb % (kRowB / 16)) * 16;
-      }
-      *reinterpret_cast<u32x4*>(dst) = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-
-  // One K step: wait for this wave's loads of step kt (later steps stay in
-  // flight), barrier (every wave's loads landed; the stage computed last
-  // step is free), refill that stage with step kt + kStages - 1, compute kt.
-  constexpr int kPerStep = DmaOperand<A_KC, BM, 1>::kPer + DmaOperand<B_KC, BN, NB>::kPer;
-  constexpr int kAhead = kStages - 1;
-  auto wait_own = [&](int ahead) {  // ahead: later steps whose loads may stay outstanding
-    if constexpr (kAhead >= 3) {
-      if (ahead >= 2) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerStep) : "memory"); return; }
-    }
-    if constexpr (kAhead >= 2) {
-      if (ahead >= 1) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerStep) : "memory"); return; }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  auto step = [&](int kt) {
-    char* cur = stg + (kt % kStages) * kStage;
-    wait_own(min(kAhead - 1, nk - 1 - kt));
-    asm volatile("s_barrier" ::: "memory");
-    if (KGROUP && tail && kt == nk - 1) {
-      clear_tail(cur);
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (kt + kAhead < nk) issue(stg + ((kt + kAhead) % kStages) * kStage, kt + kAhead);
+  load(0);
+  sa.store(smem, tid);
+  sb.store(smem + kTileA, tid);
+  lds_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * kStage;
+    char* nxt = smem + ((kt + 1) & 1) * kStage;
+    if (kt + 1 < nk) load(kt + 1);
     compute(cur);
-  };
-
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i)
-    if (i < nk) issue(stg + i * kStage, i);
-  for (int kt = 0; kt < nk; ++kt) step(kt);
+    if (kt + 1 < nk) {
+      sa.store(nxt, tid);
+      sb.store(nxt + kTileA, tid);
+    }
+    lds_barrier();
+  }
 
   // 32x32 MFMA result: lane holds column (lane % 32), rows 8*(v/4) + 4*(lane/32) + v%4.
 #pragma unroll
@@ -432,71 +385,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = n0 + wn * WN + j * 32 + (lane & 31);
-      const int rb = wm * WM + i * 32 + 4 * (lane >> 5);
-      const bool col_ok = c < p.N;
-      if constexpr (EPI == EPI_F32) {
-        // weight gradients: rows m0 + r of expert e's [M, N] fp32 matrix
-        float* c0 = reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + c;
-        float* c1 = DUAL ? reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + c : nullptr;
-        float old0[16], old1[16];
-        if (p.accum) {
+      if (c >= p.N) continue;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = m0 + rb + 8 * (v >> 2) + (v & 3);
-            const bool ok = col_ok && r < p.M;
-            old0[v] = ok ? c0[(int64_t)r * p.ldc] : 0.f;
-            if constexpr (DUAL) old1[v] = ok ? c1[(int64_t)r * p.ldc] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = m0 + rb + 8 * (v >> 2) + (v & 3);
-          if (!(col_ok && r < p.M)) continue;
-          c0[(int64_t)r * p.ldc] = p.accum ? old0[v] + acc[0][i][j][v] : acc[0][i][j][v];
-          if constexpr (DUAL)
-            c1[(int64_t)r * p.ldc] = p.accum ? old1[v] + acc[NB - 1][i][j][v] : acc[NB - 1][i][j][v];
-        }
-      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        // load eight saved (h1, h3) pairs of this 32x32 block at a time, then store
-        const uint16_t* __restrict__ X0 = reinterpret_cast<const uint16_t*>(p.X0);
-        const uint16_t* __restrict__ X1 = reinterpret_cast<const uint16_t*>(p.X1);
-        uint16_t* __restrict__ C0 = reinterpret_cast<uint16_t*>(p.C0);
-        uint16_t* __restrict__ C1 = reinterpret_cast<uint16_t*>(p.C1);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float z[8], u[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int v = 8 * h + t;
-            const int r = rb + 8 * (v >> 2) + (v & 3);
-            const bool ok = col_ok && r < valid;
-            const int64_t o = (row0 + r) * p.ldc + c;
-            z[t] = ok ? bf16_to_f32(X0[o]) : 0.f;
-            u[t] = ok ? bf16_to_f32(X1[o]) : 0.f;
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int v = 8 * h + t;
-            const int r = rb + 8 * (v >> 2) + (v & 3);
-            if (!(col_ok && r < valid)) continue;
-            const int64_t o = (row0 + r) * p.ldc + c;
-            const float da = acc[0][i][j][v];
-            const float sg = sigmoid_f(z[t]);
-            C0[o] = (uint16_t)f32_to_bf16_bits(da * u[t] * sg * (1.0f + z[t] * (1.0f - sg)));
-            C1[o] = (uint16_t)f32_to_bf16_bits(da * z[t] * sg);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = rb + 8 * (v >> 2) + (v & 3);
-          if (col_ok && r < valid)
-            epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v],
-                                      DUAL ? acc[NB - 1][i][j][v] : 0.f);
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
+        if constexpr (KGROUP) {
+          if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
+        } else {
+          if (r < valid) epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v], v1);
         }
       }
     }
-#endif
 }
 
 // ---------------------------------------------------------- fp32 kernel --
@@ -604,7 +504,7 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   TimedLaunch tl(name, s);
   if (bf16) {
     auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
-    constexpr int lds = kStages * (BM + (DUAL ? 2 : 1) * BN) * kBK * 2;  // the LDS ring
+    constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
     if (!attr) {
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
