@@ -166,6 +166,16 @@ def maxvio_beta(target: float) -> float:
     return float(table.get("beta", {}).get(f"{float(target):g}", 0.0))
 
 
+def maxvio_bias(target: float) -> Optional[np.ndarray]:
+    """Stored per-expert balancing bias for a level below the unbiased router's skew, if any."""
+    if not os.path.exists(_BETA_FILE):
+        return None
+    with open(_BETA_FILE) as f:
+        table = json.load(f)
+    vec = table.get("bias", {}).get(f"{float(target):g}")
+    return None if vec is None else np.asarray(vec, dtype=np.float32)
+
+
 def make_workload(name: str, *, S: Optional[int] = None, beta: Optional[float] = None,
                   maxvio: Optional[float] = None, host_weights: Optional[bool] = None,
                   H: Optional[int] = None, Hf: Optional[int] = None,
@@ -201,6 +211,11 @@ def make_workload(name: str, *, S: Optional[int] = None, beta: Optional[float] =
     b = 0.0
     if cfg["bias"] == "zipf":
         bias = zipf_bias(Ed, cfg["zipf_s"], seed)
+    elif cfg["bias"] == "maxvio" and beta is None and maxvio is not None \
+            and maxvio_bias(maxvio) is not None:
+        bias = maxvio_bias(maxvio)
+        if bias.shape[0] != Ed:
+            raise ValueError("stored balancing bias does not match E")
     elif cfg["bias"] == "maxvio":
         if beta is None:
             beta = maxvio_beta(maxvio) if maxvio is not None else 0.0

@@ -1,0 +1,205 @@
+"""Full-size GPU parity in the launch configuration the bench times.
+
+The layer runs exactly as in the throughput measurement (device-drawn expert
+weights, one MoELayer forward + backward at the workload's full S, H, H', E,
+K).  The oracle cannot redo the whole layer in float64 within seconds, so:
+
+* every integer output (top-K, counts, cu_seqlens, the permutation) is
+  compared bit for bit over all tokens, and xd is compared bitwise over all
+  rows (on the device, against x gathered with the oracle's permutation);
+* gates are compared over all tokens, logits over a token sample;
+* h1, h3, a, y, dy, dh1, dh3, dxd are compared on sampled rows, and out,
+  dgates, dlogits, dx on sampled tokens: the rows include each sampled
+  expert's first and last row and the rows on both sides of its 256-row tile
+  boundaries (the ragged tails), and every row of every sampled token, so the
+  oracle's combine and its backward see exactly the rows they need;
+* weight gradients are compared on sampled hidden columns of the hottest and
+  a mid-sized expert: the SwiGLU FFN is separable over its H' columns, so the
+  oracle run on the expert restricted to columns J gives dW1[:, J], dW3[:, J]
+  and dW2[J, :] exactly; experts without rows must have all-zero gradients;
+* dWg is checked against x^T dlogits over all entries (a property that holds
+  at any size; dlogits itself is checked on the token sample).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import device_expert_weights, make_workload
+from tests.moe_testutil import BF16_TOL, F32_TOL, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routing_dispatch_grouped_moe_amd import MoELayer  # noqa: E402
+from routing_dispatch_grouped_moe_amd import _lib as L  # noqa: E402
+
+TILE = 256
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _host_expert(W, e, cols=None, rows=None):
+    """Host float64 copy of one expert's matrix (optionally a column or row subset)."""
+    w = W[e]
+    if cols is not None:
+        w = w[:, torch.as_tensor(cols, device=w.device)]
+    if rows is not None:
+        w = w[torch.as_tensor(rows, device=w.device), :]
+    return w.float().cpu().numpy().astype(np.float64)
+
+
+def _sample_rows(cu, experts, rng, extra=4):
+    rows = []
+    for e in experts:
+        r0, r1 = int(cu[e]), int(cu[e + 1])
+        if r1 == r0:
+            continue
+        rows += [r0, r1 - 1]
+        for t in range(TILE, r1 - r0, TILE):
+            rows += [r0 + t - 1, r0 + t]
+        rows += list(rng.integers(r0, r1, size=extra))
+    return np.unique(np.asarray(rows, np.int64))
+
+
+FULL = [
+    ("c2_mixtral_full", "c2", None),
+    ("c3_zipf_full", "c3", None),
+    ("c4_moonep_full_maxvio0.2", "c4", 0.2),
+    ("c4_moonep_full_maxvio20", "c4", 20.0),
+]
+
+
+@pytest.mark.parametrize("cid,cfg,maxvio", FULL, ids=[c[0] for c in FULL])
+def test_fullsize_sampled(cid, cfg, maxvio):
+    _say(f"[full] {cid}: building inputs")
+    wl = make_workload(cfg, maxvio=maxvio, host_weights=False)
+    S, H, Hf, E, K = wl.S, wl.H, wl.Hf, wl.E, wl.K
+    x_t, Wg_t, dout_t = to_dev(wl.x, "bf16"), to_dev(wl.Wg, "bf16"), to_dev(wl.dout, "bf16")
+    bias_t = None if wl.bias is None else torch.from_numpy(wl.bias.astype(np.float32)).cuda()
+    W1, W3, W2 = device_expert_weights(wl.cfg, "cuda")
+    layer = MoELayer(S, H, Hf, E, K, "bf16")
+    L.moe_clear_status(layer.ws)
+    _say(f"[full] {cid}: forward + backward S={S} H={H} H'={Hf} E={E} K={K}")
+    layer.forward(x_t, Wg_t, bias_t, W1, W3, W2)
+    layer.backward(dout_t, x_t, Wg_t, W1, W3, W2)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+
+    rng = np.random.default_rng(12345)
+    logits = to_host(layer.logits)
+    # routing: every token, bit for bit
+    ts = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, size=62)]))
+    assert_close("logits[sample]", logits[ts], oracle.router_logits(wl.x[ts], wl.Wg, wl.bias),
+                 F32_TOL)
+    idx = oracle.topk_experts(logits, K)
+    np.testing.assert_array_equal(to_host(layer.topk_idx), idx, err_msg="topk_idx")
+    gates = oracle.gate_weights(logits, idx)
+    assert_close("gates", to_host(layer.gates), gates, F32_TOL)
+    counts, cu = oracle.expert_counts(idx, E)
+    np.testing.assert_array_equal(to_host(layer.counts), counts, err_msg="counts")
+    np.testing.assert_array_equal(to_host(layer.cu), cu, err_msg="cu_seqlens")
+    row_of, tok_of = oracle.dispatch_permutation(idx, E)
+    np.testing.assert_array_equal(to_host(layer.row_of), row_of, err_msg="row_of")
+    np.testing.assert_array_equal(to_host(layer.tok_of), tok_of, err_msg="tok_of")
+    assert cu[-1] == S * K
+    tok_t = torch.from_numpy(tok_of.astype(np.int64)).cuda()
+    assert torch.equal(layer.xd.view(torch.int16), x_t.view(torch.int16)[tok_t]), "xd"
+    mv = oracle.maxvio(counts)
+    _say(f"[full] {cid}: routing exact, maxvio {mv:.3f}")
+
+    # sampled experts: hottest, coldest non-empty, a median one, and a few random
+    order = np.argsort(counts, kind="stable")
+    nz = order[counts[order] > 0]
+    experts = {int(order[-1]), int(nz[0]), int(nz[len(nz) // 2])}
+    experts |= set(int(e) for e in rng.choice(nz, size=min(3, len(nz)), replace=False))
+    rows = _sample_rows(cu, sorted(experts), rng)
+    toks = np.unique(tok_of[rows])
+    if len(toks) > 24:
+        keep = np.unique(np.concatenate([tok_of[rows[[0, -1]]],
+                                         rng.choice(toks, size=22, replace=False)]))
+        toks = keep
+    ts_rows = row_of.reshape(S, K)[toks]                 # [T, K] rows of the sampled tokens
+    all_rows = np.unique(ts_rows.reshape(-1))
+    local = {int(r): i for i, r in enumerate(all_rows)}
+    expert_of_row = np.searchsorted(cu, all_rows, side="right") - 1
+
+    # forward on the sampled rows, expert by expert
+    n = len(all_rows)
+    fw = {k: np.zeros((n, Hf)) for k in ("h1", "h3", "a")}
+    fw["y"] = np.zeros((n, H))
+    Xs = np.asarray(wl.x, np.float64)[tok_of[all_rows]]
+    wcache = {}
+    for e in np.unique(expert_of_row):
+        sel = np.nonzero(expert_of_row == e)[0]
+        w = (_host_expert(W1, e), _host_expert(W3, e), _host_expert(W2, e))
+        wcache[int(e)] = sel, w
+        h1, h3, a, y = oracle.expert_ffn(Xs[sel], np.array([0, len(sel)]), w[0][None], w[1][None],
+                                         w[2][None])
+        fw["h1"][sel], fw["h3"][sel], fw["a"][sel], fw["y"][sel] = h1, h3, a, y
+    for name in ("h1", "h3", "a", "y"):
+        assert_close(f"{name}[rows]", to_host(getattr(layer, name)[torch.from_numpy(all_rows).cuda()]),
+                     fw[name], BF16_TOL)
+
+    # combine and its backward on the sampled tokens
+    rloc = np.array([local[int(r)] for r in ts_rows.reshape(-1)], np.int64)
+    out = oracle.combine(fw["y"], rloc, gates[toks])
+    assert_close("out[tokens]", to_host(layer.out)[toks], out, BF16_TOL)
+    dy_s, dg = oracle.combine_backward(np.asarray(wl.dout)[toks], fw["y"], rloc, gates[toks])
+    rows_t = torch.from_numpy(all_rows).cuda()
+    assert_close("dy[rows]", to_host(layer.dy[rows_t]), dy_s, BF16_TOL)
+    assert_close("dgates[tokens]", to_host(layer.dgates)[toks], dg, BF16_TOL)
+    dl = oracle.gate_backward(dg, logits[toks], idx[toks])
+    dl_gpu = to_host(layer.dlogits)
+    assert_close("dlogits[tokens]", dl_gpu[toks], dl, BF16_TOL)
+
+    # expert backward on the sampled rows
+    bw = {k: np.zeros((n, Hf)) for k in ("dh1", "dh3")}
+    bw["dxd"] = np.zeros((n, H))
+    for e, (sel, w) in wcache.items():
+        dxd, dh1, dh3, _, _, _ = oracle.expert_ffn_backward(
+            dy_s[sel], Xs[sel], np.array([0, len(sel)]), w[0][None], w[1][None], w[2][None],
+            fw["h1"][sel], fw["h3"][sel], fw["a"][sel], on_dW=lambda *a: None)
+        bw["dxd"][sel], bw["dh1"][sel], bw["dh3"][sel] = dxd, dh1, dh3
+    for name in ("dh1", "dh3", "dxd"):
+        assert_close(f"{name}[rows]", to_host(getattr(layer, name)[rows_t]), bw[name], BF16_TOL)
+    dx, _ = oracle.dispatch_router_backward(bw["dxd"], rloc, dl, wl.x[toks], wl.Wg, K)
+    assert_close("dx[tokens]", to_host(layer.dx)[toks], dx, BF16_TOL)
+    del wcache
+    _say(f"[full] {cid}: {n} rows / {len(toks)} tokens over {len(np.unique(expert_of_row))} experts ok")
+
+    # weight gradients on sampled hidden columns of two experts
+    pair_of_row = np.empty(S * K, np.int64)
+    pair_of_row[row_of] = np.arange(S * K)
+    for e in (int(order[-1]), int(nz[len(nz) // 2])):
+        r0, r1 = int(cu[e]), int(cu[e + 1])
+        J = np.unique(np.concatenate([[0, Hf - 1], rng.integers(0, Hf, size=6)]))
+        Xe = np.asarray(wl.x, np.float64)[tok_of[r0:r1]]
+        p = pair_of_row[r0:r1]
+        dye = gates.reshape(-1)[p][:, None] * np.asarray(wl.dout, np.float64)[p // K]
+        w1, w3, w2 = _host_expert(W1, e, cols=J), _host_expert(W3, e, cols=J), \
+            _host_expert(W2, e, rows=J)
+        cu1 = np.array([0, r1 - r0])
+        h1, h3, a, _ = oracle.expert_ffn(Xe, cu1, w1[None], w3[None], w2[None])
+        _, _, _, g1, g3, g2 = oracle.expert_ffn_backward(dye, Xe, cu1, w1[None], w3[None],
+                                                         w2[None], h1, h3, a)
+        Jt = torch.from_numpy(J).cuda()
+        assert_close(f"dW1[{e}][:,J]", to_host(layer.dW1[e][:, Jt]), g1[0], BF16_TOL)
+        assert_close(f"dW3[{e}][:,J]", to_host(layer.dW3[e][:, Jt]), g3[0], BF16_TOL)
+        assert_close(f"dW2[{e}][J,:]", to_host(layer.dW2[e][Jt, :]), g2[0], BF16_TOL)
+    empty = np.nonzero(counts == 0)[0]
+    for e in empty[:8]:
+        for g in (layer.dW1, layer.dW3, layer.dW2):
+            assert not bool(g[int(e)].any()), f"expert {e} has no rows but a nonzero gradient"
+
+    # router weight gradient: dWg = x^T dlogits over every entry
+    want = np.asarray(wl.x, np.float64).T @ dl_gpu.astype(np.float64)
+    assert_close("dWg = x^T dlogits", to_host(layer.dWg), want, F32_TOL)
+    _say(f"[full] {cid}: weight gradients ok ({len(empty)} empty experts)")
