@@ -63,8 +63,12 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.nb = (int)((S + 255) / 256);
   L.epad = (E + 15) / 16 * 16;
   L.max_tiles = (int)((R + (int64_t)E * (kGemmBM - 1)) / kGemmBM);
+  // dWg row items: about 2048 (item, 2048-column chunk) blocks whatever the skew
   const int hblocks = (H + 2047) / 2048;
-  L.dwg_splits = std::max(1, std::min(64, (1024 + E * hblocks - 1) / (E * hblocks)));
+  int rb = 16;
+  while (rb < 256 && (int64_t)rb * 2 * 2048 <= R * hblocks) rb *= 2;
+  L.dwg_rb = rb;
+  L.dwg_max_items = (int)((R + (int64_t)E * (rb - 1)) / rb);
   size_t off = 0;
   L.status = off; off = align256(off + 4);
   L.wgT = off; off = align256(off + (size_t)L.epad * H * esz);
@@ -74,7 +78,9 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.tiles = off; off = align256(off + (size_t)std::max(L.max_tiles, 1) * 8);
   L.ntiles = off; off = align256(off + 4);
   L.dl_row = off; off = align256(off + (size_t)std::max<int64_t>(R, 1) * 4);
-  L.dwg_part = off; off = align256(off + (size_t)L.dwg_splits * E * H * 4);
+  L.dwg_items = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * 16);
+  L.dwg_estart = off; off = align256(off + (size_t)(E + 1) * 4);
+  L.dwg_part = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * H * 4);
   L.total = off;
   return L;
 }

@@ -14,8 +14,8 @@
 // (8 bf16) of the token's rows, accumulates in fp32 and writes 16-byte
 // pieces, so every row read and write is a full coalesced 1-KB wave access.
 // The router-weight gradient reduces over each expert's contiguous rows in
-// row order (deterministic), split over row ranges into fp32 partials that a
-// second kernel adds in split order.
+// row order (deterministic), cut into row items of bounded size so a hot
+// expert spreads over many blocks; a second kernel adds the items in order.
 #include "dev_common.h"
 #include "launch.h"
 #include "moe.h"
@@ -228,63 +228,134 @@ void launch_dx(const void* dxd, const int32_t* row_of, const int32_t* idx, const
                        wgT, dx, (int)S, H, E, K, R);
 }
 
-// Partial router-weight gradient: block (e, h-chunk of 2048, split) sums
-// dl_row[r] * xd[r, h..h+8) over its share of expert e's rows, in row order.
+// Router-weight gradient, balanced over skewed experts.  Each expert's rows
+// are cut into items of at most rb rows (one table entry per item, built on
+// the device from cu_seqlens, so no host sync); block (item, 2048-column
+// chunk) sums dl_row[r] * xd[r, h..h+8) over the item's rows in row order
+// into an fp32 partial; the reduce adds each expert's items in item order
+// (deterministic) and writes dWg [H, E] through an LDS transpose so both the
+// partial reads and the dWg writes are contiguous.
+__global__ __launch_bounds__(1024) void dwg_items_kernel(const int32_t* __restrict__ cu, int E,
+                                                         int R, int rb, int max_items,
+                                                         int4* __restrict__ items,
+                                                         int32_t* __restrict__ estart) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  // rows outside [0, R) of a malformed cu_seqlens are never visited
+  const int r0 = e < E ? min(max(cu[e], 0), R) : 0;
+  const int c = e < E ? max(0, min(cu[e + 1], R) - r0) : 0;
+  const int nt = (c + rb - 1) / rb;
+  sh[e] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = e >= o ? sh[e - o] : 0;
+    __syncthreads();
+    sh[e] += add;
+    __syncthreads();
+  }
+  const int start = sh[e] - nt, total = sh[1023];
+  for (int t = 0; t < nt && start + t < max_items; ++t)
+    items[start + t] = make_int4(e, r0 + t * rb, min(rb, c - t * rb), 0);
+  if (e < E) estart[e] = min(start, max_items);
+  if (e == 0) estart[E] = min(total, max_items);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void dwg_partial_kernel(const void* __restrict__ xd,
-                                                          const int32_t* __restrict__ cu,
+                                                          const int4* __restrict__ items,
+                                                          const int32_t* __restrict__ estart,
                                                           const float* __restrict__ dl_row,
-                                                          float* __restrict__ part, int H, int E,
-                                                          int splits) {
-  const int e = blockIdx.x, sp = blockIdx.z;
+                                                          float* __restrict__ part, int H, int E) {
+  const int it = blockIdx.x;
+  if (it >= estart[E]) return;
   const int h = blockIdx.y * 2048 + threadIdx.x * 8;
   if (h >= H) return;
-  const int r0 = cu[e], n = cu[e + 1] - r0;
-  const int a = r0 + (int)((int64_t)n * sp / splits), b = r0 + (int)((int64_t)n * (sp + 1) / splits);
+  const int4 item = items[it];
+  const int r0 = item.y, n = item.z;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = a; r < b; ++r) {
-    const float d = dl_row[r];
+  int r = 0;
+  for (; r + 4 <= n; r += 4) {  // four rows in flight per step; sums stay in row order
+    float v[4][8], d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d[j] = dl_row[r0 + r + j];
+      load8<BF16>(xd, (int64_t)(r0 + r + j) * H + h, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += d[j] * v[j][i];
+  }
+  for (; r < n; ++r) {
     float v[8];
-    load8<BF16>(xd, (int64_t)r * H + h, v);
+    const float d = dl_row[r0 + r];
+    load8<BF16>(xd, (int64_t)(r0 + r) * H + h, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += d * v[i];
   }
-  float* o = part + ((size_t)sp * E + e) * H + h;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = acc[i];
+  float* o = part + (size_t)it * H + h;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// Block (64 columns h, 16 experts): 256 threads each sum 4 columns of one
+// expert over its items, then write 4 experts of one column.
 __global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict__ part,
+                                                         const int32_t* __restrict__ estart,
                                                          float* __restrict__ dWg, int H, int E,
-                                                         int splits, int accum) {
-  const int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;  // over [H, E], e fastest
-  if (i >= (int64_t)H * E) return;
-  const int h = (int)(i / E), e = (int)(i % E);
-  float v = 0.f;
-  for (int sp = 0; sp < splits; ++sp) v += part[((size_t)sp * E + e) * H + h];
-  dWg[i] = accum ? dWg[i] + v : v;
+                                                         int accum) {
+  __shared__ float tile[16][65];
+  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 16;
+  const int t = threadIdx.x;
+  {
+    const int el = t >> 4, hs = (t & 15) * 4, e = e0 + el, h = h0 + hs;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < E && h < H) {
+      const int i0 = estart[e], i1 = estart[e + 1];
+      for (int i = i0; i < i1; ++i) {
+        const float4 p = *reinterpret_cast<const float4*>(part + (size_t)i * H + h);
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+      }
+    }
+    tile[el][hs] = v.x; tile[el][hs + 1] = v.y; tile[el][hs + 2] = v.z; tile[el][hs + 3] = v.w;
+  }
+  __syncthreads();
+  const int hl = t >> 2, es = (t & 3) * 4, h = h0 + hl;
+  if (h >= H) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + es + j;
+    if (e >= E) break;
+    float* o = dWg + (int64_t)h * E + e;
+    *o = accum ? *o + tile[es + j][hl] : tile[es + j][hl];
+  }
 }
 
 void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* dWg,
                 const WsLayout& L, char* ws, int64_t R, int H, int E, bool accum, bool bf16,
                 hipStream_t s) {
-  (void)R;
+  int4* items = reinterpret_cast<int4*>(ws + L.dwg_items);
+  int32_t* estart = reinterpret_cast<int32_t*>(ws + L.dwg_estart);
   float* part = reinterpret_cast<float*>(ws + L.dwg_part);
-  dim3 grid(E, (H + 2047) / 2048, L.dwg_splits);
   {
+    TimedLaunch tl("router_dWg_items", s);
+    hipLaunchKernelGGL(dwg_items_kernel, dim3(1), dim3(1024), 0, s, cu, E, (int)R, L.dwg_rb,
+                       L.dwg_max_items, items, estart);
+  }
+  if (L.dwg_max_items > 0) {
     TimedLaunch tl("router_dWg_partial", s);
+    dim3 grid(L.dwg_max_items, (H + 2047) / 2048);
     if (bf16)
-      hipLaunchKernelGGL(dwg_partial_kernel<true>, grid, dim3(256), 0, s, xd, cu, dl_row, part, H, E,
-                         L.dwg_splits);
+      hipLaunchKernelGGL(dwg_partial_kernel<true>, grid, dim3(256), 0, s, xd, items, estart, dl_row,
+                         part, H, E);
     else
-      hipLaunchKernelGGL(dwg_partial_kernel<false>, grid, dim3(256), 0, s, xd, cu, dl_row, part, H,
-                         E, L.dwg_splits);
+      hipLaunchKernelGGL(dwg_partial_kernel<false>, grid, dim3(256), 0, s, xd, items, estart,
+                         dl_row, part, H, E);
   }
   {
     TimedLaunch tl("router_dWg_reduce", s);
-    const int64_t n = (int64_t)H * E;
-    hipLaunchKernelGGL(dwg_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
-                       dWg, H, E, L.dwg_splits, accum ? 1 : 0);
+    hipLaunchKernelGGL(dwg_reduce_kernel, dim3((H + 63) / 64, (E + 15) / 16), dim3(256), 0, s, part,
+                       estart, dWg, H, E, accum ? 1 : 0);
   }
 }
 

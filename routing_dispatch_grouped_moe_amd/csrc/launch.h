@@ -28,12 +28,15 @@ struct WsLayout {
   size_t tiles;       // grouped GEMM: [max_tiles] int2 (expert, first row) per M tile
   size_t ntiles;      // int32 number of valid M tiles
   size_t dl_row;      // [R] fp32 dlogit of each dispatched row
-  size_t dwg_part;    // [dwg_splits, E, H] fp32 partial router-weight gradients
+  size_t dwg_items;   // [dwg_max_items] int4 (expert, first row, rows, 0) row items of dWg
+  size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
+  size_t dwg_part;    // [dwg_max_items, H] fp32 partial router-weight gradient per item
   size_t total;
   int nb;             // dispatch blocks of 256 tokens
   int epad;           // E rounded up to 16
   int max_tiles;      // upper bound on M tiles over all experts
-  int dwg_splits;     // row splits of the router-weight gradient
+  int dwg_rb;         // rows per dWg item (a power of two, 16..256)
+  int dwg_max_items;  // upper bound on dWg items over all experts
 };
 WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
 
