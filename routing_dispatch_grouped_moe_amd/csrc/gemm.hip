@@ -35,6 +35,8 @@
 //
 // The fp32 storage type (the tiny fp32 workload) uses a plain FMA kernel
 // with the same tile table and epilogues.
+#include <type_traits>
+
 #include "dev_common.h"
 #include "launch.h"
 
@@ -91,6 +93,47 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
     if constexpr (DUAL) {
       float* c1 = reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o;
       *c1 = p.accum ? *c1 + v1 : v1;
+    }
+  }
+}
+
+// The same epilogues on four consecutive columns (col % 4 == 0) of one row:
+// one 8-byte bf16 or 16-byte fp32 access per operand instead of four.
+template <int EPI, bool DUAL>
+__device__ __forceinline__ void epilogue4(const GemmArgs& p, int e, int64_t row, int col,
+                                          const float (&v0)[4], const float (&v1)[4]) {
+  const int64_t o = row * p.ldc + col;
+  if constexpr (EPI == EPI_STORE) {
+    store4_bf16(p.C0, o, v0);
+  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+    float a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = silu_f(v0[t]) * v1[t];
+    store4_bf16(p.C0, o, v0);
+    store4_bf16(p.C1, o, v1);
+    store4_bf16(p.C2, o, a);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    float z[4], u[4], d1[4], d3[4];
+    load4_bf16(p.X0, o, z);
+    load4_bf16(p.X1, o, u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sg = sigmoid_f(z[t]);
+      d1[t] = v0[t] * u[t] * sg * (1.0f + z[t] * (1.0f - sg));
+      d3[t] = v0[t] * z[t] * sg;
+    }
+    store4_bf16(p.C0, o, d1);
+    store4_bf16(p.C1, o, d3);
+  } else {
+    float4* c0 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + o);
+    float4 w0 = make_float4(v0[0], v0[1], v0[2], v0[3]);
+    if (p.accum) { const float4 q = *c0; w0.x += q.x; w0.y += q.y; w0.z += q.z; w0.w += q.w; }
+    *c0 = w0;
+    if constexpr (DUAL) {
+      float4* c1 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o);
+      float4 w1 = make_float4(v1[0], v1[1], v1[2], v1[3]);
+      if (p.accum) { const float4 q = *c1; w1.x += q.x; w1.y += q.y; w1.z += q.z; w1.w += q.w; }
+      *c1 = w1;
     }
   }
 }
@@ -194,19 +237,19 @@ __device__ __forceinline__ u32x4 frag_km(const char* tile, int col_base, int kk,
 // One operand tile of one K step, staged global -> registers -> LDS.
 //   KC:  stored [rows][K] in HBM, tile rows [0, ROWS), k [k0, k0+64)
 //   !KC: stored [K][cols] in HBM, tile k rows [k0, k0+64), cols [c0, c0+ROWS)
-template <bool KC, int ROWS, int NOPS>
+template <bool KC, int ROWS, int NOPS, int THREADS = kThreads>
 struct Stager {
   static constexpr int kChunks = ROWS * (kBK / 8);          // 16-byte chunks per operand
-  static constexpr int kPer = NOPS * kChunks / kThreads;    // per thread
-  static_assert(NOPS * kChunks % kThreads == 0, "tile not a multiple of the block");
+  static constexpr int kPer = NOPS * kChunks / THREADS;     // per thread
+  static_assert(kChunks % THREADS == 0, "operand tile not a multiple of the block");
   u32x4 r[kPer];
 
   __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t (&rs)[NOPS], int64_t ld,
                                        int base, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = tid + kThreads * i;
-      const int op = q / kChunks, lq = q % kChunks;
+      // operand index from the unrolled step alone (uniform), chunk from the thread
+      const int op = (THREADS * i) / kChunks, lq = (THREADS * i) % kChunks + tid;
       int64_t el;
       if constexpr (KC) {
         el = (int64_t)(base + (lq >> 3)) * ld + k0 + (lq & 7) * 8;
@@ -220,8 +263,7 @@ struct Stager {
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = tid + kThreads * i;
-      const int op = q / kChunks, lq = q % kChunks;
+      const int op = (THREADS * i) / kChunks, lq = (THREADS * i) % kChunks + tid;
       char* t = lds + op * (ROWS * kBK * 2);
       uint32_t off;
       if constexpr (KC) {
@@ -399,6 +441,300 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     }
 }
 
+// Direct global -> LDS staging of one operand tile per K step with
+// buffer_load ... lds: each wave instruction moves 1 KB, lane l's 16 bytes
+// landing at +16 l, so the swizzled LDS layouts above are produced by
+// choosing which global chunk each lane fetches.  Lane offsets are for K
+// step 0 and loop invariant; a step's K offset moves the buffer descriptor's
+// base instead (scalar work), and the descriptor's range still bounds every
+// read (past the end reads zero).
+//   KC:  stored [rows][K] in HBM, LDS tile [ROWS][kBK]
+//   !KC: stored [K][cols] in HBM, LDS tile [kBK][ROWS]
+
+template <bool KC, int ROWS, int NOPS, int WAVES>
+struct DmaOperand {
+  static constexpr int kInstr = NOPS * ROWS * kBK * 2 / 1024;  // 1-KB wave instructions per step
+  static constexpr int kPer = kInstr / WAVES;                  // per wavefront
+  static_assert(kInstr % (WAVES * NOPS) == 0, "operand tile not a multiple of the waves");
+  uint32_t voff[kPer];
+
+  __device__ __forceinline__ void init(int64_t ld, int base, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ins = w * kPer + i;
+      const int op = ins / (kInstr / NOPS);
+      const int P = (ins - op * (kInstr / NOPS)) * 64 + lane;  // physical 16-byte chunk
+      int64_t el;
+      if constexpr (KC) {
+        constexpr int cpr = kBK / 8;
+        const int row = P / cpr;
+        el = (int64_t)(base + row) * ld + ((P % cpr) ^ ((row >> 1) & 7)) * 8;
+      } else {
+        constexpr int cpr = ROWS / 8;
+        const int k = P / cpr;
+        el = (int64_t)k * ld + base + ((P % cpr) ^ (4 * (k & 3)) ^ (2 * ((k >> 3) & 1))) * 8;
+      }
+      voff[i] = (uint32_t)(el * 2);
+    }
+  }
+  // Instruction i of this wavefront's loads of the step whose descriptors
+  // are rsrc[]: issued from inline assembly, so the compiler does not treat
+  // it as an LDS store and never makes LDS reads wait for it; the kernel
+  // waits for these loads explicitly (vmcnt) before the barrier that
+  // publishes their stage, and only ever targets a stage nobody reads.
+  __device__ __forceinline__ void issue_one(int i, const u32x4 (&rsrc)[NOPS], char* lds, int w) const {
+    const int ins = w * kPer + i;
+    const int op = ins / (kInstr / NOPS);
+    char* dst = lds + (ins - op * (kInstr / NOPS)) * 1024 + op * (ROWS * kBK * 2);
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff[i]), "s"(rsrc[op]), "s"(m0) : "m0");
+  }
+  // descriptor words of operand op for the K step at element offset k0
+  __device__ __forceinline__ void rsrc_for(const uint16_t* const (&base)[NOPS], uint32_t bytes,
+                                           int64_t ld, int k0, u32x4 (&rsrc)[NOPS]) const {
+    const uint32_t kadd = KC ? (uint32_t)k0 * 2u : (uint32_t)((int64_t)k0 * ld * 2);
+    const uint32_t left = __builtin_amdgcn_readfirstlane(bytes - min(kadd, bytes));
+#pragma unroll
+    for (int op = 0; op < NOPS; ++op) {
+      const uint64_t a = (uint64_t)(uintptr_t)(reinterpret_cast<const char*>(base[op]) + kadd);
+      rsrc[op][0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+      rsrc[op][1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+      rsrc[op][2] = left;
+      rsrc[op][3] = 0x00020000u;
+    }
+  }
+};
+
+// ------------------------------------------------ one wavefront per SIMD --
+// Four wavefronts (2 x 2) over the same 256 x 256 tile, each owning 128 x 128
+// (4 x 4 MFMA blocks, or 4 x 2 per operand for the dual-B products): 256
+// fp32 accumulators per lane in the accumulation registers, which takes the
+// whole register file of a SIMD (one wavefront per SIMD) and does twice the
+// MFMA work per LDS byte of the eight-wavefront form.  Operand tiles arrive
+// in LDS by direct loads (no staging registers, no LDS store instructions)
+// into two 64-KB stages, one LDS object each.  A K step is four K16 slices,
+// each in a pinned issue order (MFMA, then the next slice's fragment read,
+// then possibly one direct load); the second half of the next step's loads
+// goes out in slice 0, the barrier follows slice 2 once this wavefront's
+// loads of the next step have landed, and slice 3 sends the first half of
+// the loads of the step after next into the stage just finished.  The MFMA
+// takes the B fragment as its first operand, so each lane ends with four
+// consecutive output columns per register group and the epilogue writes
+// 8- or 16-byte pieces.
+constexpr int kThreads4 = 256;
+
+template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
+__global__ __launch_bounds__(kThreads4) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_w4_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int WM = BM / 2, WN = BN / 2;      // wavefront tile (per B operand)
+  constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
+  constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
+  constexpr int kStage = kTileA + NB * kTileB;
+  // one LDS object per stage: the compiler can then tell that direct loads
+  // into one stage never alias fragment reads of the other, and does not make
+  // those reads wait for the loads
+  __shared__ __attribute__((aligned(1024))) char stage0[kStage];
+  __shared__ __attribute__((aligned(1024))) char stage1[kStage];
+
+  int e, valid, m0, n0;
+  int64_t row0;
+  if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+
+  // operand bases (A segments, B operands) and their byte ranges
+  const uint16_t* a_ptr[TWOSEG ? 2 : 1];
+  const uint16_t* b_ptr[(DUAL || TWOSEG) ? 2 : 1];
+  uint32_t a_bytes, b_bytes;
+  int a_base, b_base, nk;
+  const int nk_seg = KGROUP ? 0 : p.K / kBK;
+  if constexpr (KGROUP) {
+    if (valid == 0) {
+      if (!p.accum) {
+        for (int i = tid; i < BM * BN; i += kThreads4) {
+          const int r = i / BN, c = i % BN;
+          if (m0 + r < p.M && n0 + c < p.N) epilogue<EPI, true, DUAL>(p, e, m0 + r, n0 + c, 0.f, 0.f);
+        }
+      }
+      return;
+    }
+    a_ptr[0] = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
+    b_ptr[0] = reinterpret_cast<const uint16_t*>(p.B0) + row0 * p.ldb;
+    if constexpr (DUAL) b_ptr[1] = reinterpret_cast<const uint16_t*>(p.B1) + row0 * p.ldb;
+    a_bytes = (uint32_t)((int64_t)valid * p.lda * 2);
+    b_bytes = (uint32_t)((int64_t)valid * p.ldb * 2);
+    a_base = m0;
+    b_base = n0;
+    nk = (valid + kBK - 1) / kBK;
+  } else {
+    a_ptr[0] = reinterpret_cast<const uint16_t*>(p.A0) + row0 * p.lda;
+    if constexpr (TWOSEG) a_ptr[1] = reinterpret_cast<const uint16_t*>(p.A1) + row0 * p.lda;
+    b_ptr[0] = reinterpret_cast<const uint16_t*>(p.B0) + (int64_t)e * p.sBe;
+    if constexpr (DUAL || TWOSEG) b_ptr[1] = reinterpret_cast<const uint16_t*>(p.B1) + (int64_t)e * p.sBe;
+    a_bytes = (uint32_t)((int64_t)valid * p.lda * 2);
+    b_bytes = (uint32_t)((int64_t)p.N * p.K * 2);
+    a_base = 0;
+    b_base = n0;
+    nk = TWOSEG ? 2 * nk_seg : nk_seg;
+  }
+
+  DmaOperand<A_KC, BM, 1, 4> da;
+  DmaOperand<B_KC, BN, NB, 4> db;
+  da.init(p.lda, a_base, w, lane);
+  db.init(p.ldb, b_base, w, lane);
+  // descriptors of K step kt (scalar work)
+  auto step_rsrc = [&](int kt, u32x4 (&ra)[1], u32x4 (&rb)[NB]) {
+    int seg = 0, k0 = kt * kBK;
+    if constexpr (TWOSEG) {
+      seg = kt >= nk_seg ? 1 : 0;
+      k0 = (kt - seg * nk_seg) * kBK;
+    }
+    const uint16_t* const pa[1] = {seg ? a_ptr[TWOSEG ? 1 : 0] : a_ptr[0]};
+    da.rsrc_for(pa, a_bytes, p.lda, k0, ra);
+    if constexpr (DUAL) {
+      db.rsrc_for(b_ptr, b_bytes, p.ldb, k0, rb);
+    } else {
+      const uint16_t* const pb[1] = {seg ? b_ptr[(DUAL || TWOSEG) ? 1 : 0] : b_ptr[0]};
+      db.rsrc_for(pb, b_bytes, p.ldb, k0, rb);
+    }
+  };
+  constexpr int kDmaA = DmaOperand<A_KC, BM, 1, 4>::kPer;
+  auto issue_one = [&](int t, const u32x4 (&ra)[1], const u32x4 (&rb)[NB], char* st) {
+    if (t < kDmaA) da.issue_one(t, ra, st, w);
+    else db.issue_one(t - kDmaA, rb, st + kTileA, w);
+  };
+  f32x16 acc[NB][MI][NJ];
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][i][j][v] = 0.f;
+
+  u32x4 af0[MI], bf0[NB][NJ], af1[MI], bf1[NB][NJ];
+  // fragment f of slice kk: f < MI an A fragment, else B fragment (q, j)
+  auto read_frag = [&](const char* st, int kk, int f, u32x4 (&af)[MI], u32x4 (&bfr)[NB][NJ]) {
+    if (f < MI) {
+      if constexpr (A_KC) af[f] = frag_kc(st, wm * WM + f * 32, kk, lane);
+      else af[f] = frag_km<BM>(st, wm * WM + f * 32, kk, lane);
+    } else {
+      const int q = (f - MI) / NJ, j = (f - MI) % NJ;
+      const char* t = st + kTileA + q * kTileB;
+      if constexpr (B_KC) bfr[q][j] = frag_kc(t, wn * WN + j * 32, kk, lane);
+      else bfr[q][j] = frag_km<BN>(t, wn * WN + j * 32, kk, lane);
+    }
+  };
+  constexpr int kMfma = MI * NB * NJ;
+  constexpr int kFrag = MI + NB * NJ;
+  constexpr int kDma = kDmaA + DmaOperand<B_KC, BN, NB, 4>::kPer;
+  constexpr int kHalf = kDma / 2;
+  static_assert(kFrag <= kMfma && kHalf <= kMfma && kMfma % kHalf == 0, "slice interleave");
+
+  // One K16 slice in a pinned issue order: MFMA t on the current fragments,
+  // then fragment t of the next slice (from stage rd), then every
+  // (kMfma / kHalf)-th MFMA one direct load (instruction d0 + n of the step
+  // whose descriptors are ra/rb, into stage ds).  The address unit accepts
+  // one such 1-KB load about every 16 cycles, so a step's loads are spread
+  // over two slices rather than bunched.
+  auto slice = [&](const u32x4 (&afc)[MI], const u32x4 (&bfc)[NB][NJ], const char* rd, int rd_kk,
+                   u32x4 (&afn)[MI], u32x4 (&bfn)[NB][NJ], const u32x4 (&ra)[1],
+                   const u32x4 (&rb)[NB], char* ds, int d0, auto dma_tag) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+#pragma unroll
+    for (int t = 0; t < kMfma; ++t) {
+      const int i = t / (NB * NJ), q = (t / NJ) % NB, j = t % NJ;
+      acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, bfc[q][j]), __builtin_bit_cast(bf16x8, afc[i]), acc[q][i][j],
+          0, 0, 0);
+      if (rd != nullptr && t < kFrag) read_frag(rd, rd_kk, t, afn, bfn);
+      if constexpr (DMA)
+        if (t % (kMfma / kHalf) == 0) issue_one(d0 + t / (kMfma / kHalf), ra, rb, ds);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // Step kt (stage CUR holds its data; the first half of step kt+1's loads
+  // are in flight):
+  //   slice 0   second half of step kt+1's loads into the other stage
+  //   slices 1-2
+  //   barrier   after this wavefront's loads of step kt+1 landed (vmcnt)
+  //   slice 3   first half of step kt+2's loads into stage CUR, which every
+  //             wavefront finished reading before the barrier
+  // Loads past the last step stay inside the descriptors' ranges and go to
+  // a stage that is not read again, so the loop has no tail copy; the step
+  // count is rounded up to even for the two-stage unroll (K-grouped products
+  // then run one step of zero rows when their row count needs an odd number).
+  auto step = [&](int kt, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    char* cur = CUR ? stage1 : stage0;
+    char* nxt = CUR ? stage0 : stage1;
+    u32x4 ra1[1], rb1[NB], ra2[1], rb2[NB];
+    step_rsrc(kt + 1, ra1, rb1);
+    step_rsrc(kt + 2, ra2, rb2);
+    slice(af0, bf0, cur, 1, af1, bf1, ra1, rb1, nxt, kHalf, T{});
+    slice(af1, bf1, cur, 2, af0, bf0, ra1, rb1, nxt, 0, F{});
+    slice(af0, bf0, cur, 3, af1, bf1, ra1, rb1, nxt, 0, F{});
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    slice(af1, bf1, nxt, 0, af0, bf0, ra2, rb2, cur, 0, T{});
+  };
+
+  {
+    u32x4 ra[1], rb[NB];
+    step_rsrc(0, ra, rb);
+#pragma unroll
+    for (int t = 0; t < kDma; ++t) issue_one(t, ra, rb, stage0);
+    step_rsrc(1, ra, rb);
+#pragma unroll
+    for (int t = 0; t < kHalf; ++t) issue_one(t, ra, rb, stage1);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kHalf) : "memory");
+#pragma unroll
+  for (int f = 0; f < kFrag; ++f) read_frag(stage0, 0, f, af0, bf0);
+  const int nk2 = (nk + 1) & ~1;
+  for (int kt = 0; kt < nk2; kt += 2) {
+    step(kt, I0{});
+    step(kt + 1, I1{});
+  }
+  // no direct load may still be writing LDS when the block exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // With the B fragment as the MFMA's first operand the 32x32 result is
+  // transposed: lane l holds row (l % 32) of the block and, for v = 4g + t,
+  // column 8 g + 4 (l / 32) + t, i.e. four consecutive columns per g.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * WM + i * 32 + (lane & 31);
+    const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
+    if (!row_ok) continue;
+    const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        if (c >= p.N) continue;
+        float v0[4], v1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v0[t] = acc[0][i][j][4 * g + t];
+          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
+        }
+        epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+      }
+  }
+#endif
+}
+
 // ---------------------------------------------------------- fp32 kernel --
 // M tile of kGemmBM rows x 32 columns; thread (tid % 32) owns a column,
 // rows tid/32 + 8 i.
@@ -487,6 +823,7 @@ void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hi
 }
 
 // -------------------------------------------------------------- launches --
+constexpr bool kUseW4 = true;
 template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
   static_assert(KGROUP || BM == kGemmBM, "M-grouped tiles follow the tile table");
@@ -503,15 +840,24 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   if (blocks <= 0) return;
   TimedLaunch tl(name, s);
   if (bf16) {
-    auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
     constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
-    if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      attr = true;
+    if constexpr (kUseW4 && !KGROUP && EPI != EPI_SWIGLU_BWD) {
+      // the one-wavefront-per-SIMD form for the M-grouped products; the
+      // weight gradients and the SwiGLU-backward product keep the eight-
+      // wavefront form (their extra live registers do not fit one SIMD's file
+      // next to 256 accumulators)
+      auto kern = gemm_bf16_w4_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads4), 0, s, p);
+    } else {
+      auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
+      if (!attr) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        attr = true;
+      }
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, p);
     }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, p);
   } else {
     hipLaunchKernelGGL((gemm_f32_kernel<A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>), dim3(blocks),
                        dim3(256), 0, s, p);
