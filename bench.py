@@ -271,7 +271,7 @@ def main():
     if not args.no_cpu_baseline:
         del x, Wg, dout, W1, W3, W2, layer, moe
         torch.cuda.empty_cache()
-        default_sample = {"c1": 64, "c2": 2048, "c3": 1024, "c4": 16, "c5": 512}[args.config]
+        default_sample = {"c1": 64, "c2": 4096, "c3": 1024, "c4": 16, "c5": 512}[args.config]
         say(f"GPU part done ({ms_per_step:.2f} ms/step); timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.config, args.maxvio,
                                            args.cpu_sample or default_sample)

@@ -229,12 +229,15 @@ void launch_dx(const void* dxd, const int32_t* row_of, const int32_t* idx, const
 }
 
 // Router-weight gradient, balanced over skewed experts.  Each expert's rows
-// are cut into items of at most rb rows (one table entry per item, built on
-// the device from cu_seqlens, so no host sync); block (item, 2048-column
-// chunk) sums dl_row[r] * xd[r, h..h+8) over the item's rows in row order
-// into an fp32 partial; the reduce adds each expert's items in item order
+// are cut into items of about rb rows, at most 64 per expert (a hot
+// expert's items grow instead), with one table entry per item built on the
+// device from cu_seqlens, so no host sync.  Block (item, 2048-column chunk)
+// sums dl_row[r] * xd[r, h..h+8) over the item's rows in row order into an
+// fp32 partial; the reduce adds each expert's items in item order
 // (deterministic) and writes dWg [H, E] through an LDS transpose so both the
 // partial reads and the dWg writes are contiguous.
+constexpr int kDwgMaxItems = 64;
+
 __global__ __launch_bounds__(1024) void dwg_items_kernel(const int32_t* __restrict__ cu, int E,
                                                          int R, int rb, int max_items,
                                                          int4* __restrict__ items,
@@ -244,7 +247,10 @@ __global__ __launch_bounds__(1024) void dwg_items_kernel(const int32_t* __restri
   // rows outside [0, R) of a malformed cu_seqlens are never visited
   const int r0 = e < E ? min(max(cu[e], 0), R) : 0;
   const int c = e < E ? max(0, min(cu[e + 1], R) - r0) : 0;
-  const int nt = (c + rb - 1) / rb;
+  // at most kDwgMaxItems items per expert (a hot expert's items grow
+  // instead), so the reduce never walks more than that many partials
+  const int nt = min((c + rb - 1) / rb, kDwgMaxItems);
+  const int rpi = nt > 0 ? (c + nt - 1) / nt : 0;  // rows per item
   sh[e] = nt;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(1024) void dwg_items_kernel(const int32_t* __restri
   }
   const int start = sh[e] - nt, total = sh[1023];
   for (int t = 0; t < nt && start + t < max_items; ++t)
-    items[start + t] = make_int4(e, r0 + t * rb, min(rb, c - t * rb), 0);
+    items[start + t] = make_int4(e, r0 + t * rpi, min(rpi, c - t * rpi), 0);
   if (e < E) estart[e] = min(start, max_items);
   if (e == 0) estart[E] = min(total, max_items);
 }

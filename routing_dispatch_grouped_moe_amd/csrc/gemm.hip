@@ -291,6 +291,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
+  // bf16 outputs take the transposed MFMA result (four consecutive columns
+  // per lane, 8-byte pieces); the fp32 weight gradients keep the direct one,
+  // where each 4-byte store instruction writes two whole 128-byte rows,
+  // which suits these write-bound products better than 16-byte pieces
+  // scattered over 32 rows
+  constexpr bool kSwapAB = EPI != EPI_F32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
@@ -396,9 +402,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
         for (int q = 0; q < NB; ++q)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[q][j]),
-                acc[q][i][j], 0, 0, 0);
+            acc[q][i][j] = kSwapAB
+                ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfr[q][j]),
+                                                          __builtin_bit_cast(bf16x8, af[i]),
+                                                          acc[q][i][j], 0, 0, 0)
+                : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                          __builtin_bit_cast(bf16x8, bfr[q][j]),
+                                                          acc[q][i][j], 0, 0, 0);
       // keep one K16 slice of fragments live at a time (register budget of
       // two wavefronts per SIMD)
       __builtin_amdgcn_sched_barrier(0);
@@ -421,24 +431,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     lds_barrier();
   }
 
-  // 32x32 MFMA result: lane holds column (lane % 32), rows 8*(v/4) + 4*(lane/32) + v%4.
+  if constexpr (kSwapAB) {
+    // transposed 32x32 result: lane l holds row (l % 32) and, for v = 4g + t,
+    // column 8 g + 4 (l / 32) + t
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
+      const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = n0 + wn * WN + j * 32 + (lane & 31);
-      if (c >= p.N) continue;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
-        if constexpr (KGROUP) {
-          if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
-        } else {
-          if (r < valid) epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v], v1);
+        for (int g = 0; g < 4; ++g) {
+          const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          float v0[4], v1[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v0[t] = acc[0][i][j][4 * g + t];
+            v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
+          }
+          if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+        }
+    }
+  } else {
+    // direct 32x32 result: lane holds column (lane % 32), rows 8 (v/4) + 4 (lane/32) + v%4
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = n0 + wn * WN + j * 32 + (lane & 31);
+        if (c >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
+          if constexpr (KGROUP) {
+            if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
+          } else {
+            if (r < valid) epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v], v1);
+          }
         }
       }
-    }
+  }
 }
 
 // Direct global -> LDS staging of one operand tile per K step with
