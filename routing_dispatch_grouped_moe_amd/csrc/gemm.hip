@@ -42,6 +42,20 @@
 
 namespace moe {
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled by construction (a
+// loop the optimiser leaves rolled would index the accumulator array at run
+// time and move it to scratch memory)
+template <int B, int E>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      StaticFor<B + 1, E>::run(f);
+    }
+  }
+};
+
 constexpr int kBK = 64;
 constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
 constexpr int kGroupM = 4;  // M tiles walked together (n fastest inside the group)
@@ -88,11 +102,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
     store1<BF16>(p.C0, o, v0 * u * sg * (1.0f + z * (1.0f - sg)));
     store1<BF16>(p.C1, o, v0 * z * sg);
   } else {
+    // weight gradients are written once and not read again in the layer:
+    // non-temporal stores keep them from displacing operand tiles in L2
     float* c0 = reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + o;
-    *c0 = p.accum ? *c0 + v0 : v0;
+    __builtin_nontemporal_store(p.accum ? *c0 + v0 : v0, c0);
     if constexpr (DUAL) {
       float* c1 = reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o;
-      *c1 = p.accum ? *c1 + v1 : v1;
+      __builtin_nontemporal_store(p.accum ? *c1 + v1 : v1, c1);
     }
   }
 }
@@ -434,25 +450,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   if constexpr (kSwapAB) {
     // transposed 32x32 result: lane l holds row (l % 32) and, for v = 4g + t,
     // column 8 g + 4 (l / 32) + t
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
+StaticFor<0, MI>::run([&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value;
       const int r = wm * WM + i * 32 + (lane & 31);
       const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
       const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
+      StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
+        constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
+        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        float v0[4], v1[4];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          float v0[4], v1[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v0[t] = acc[0][i][j][4 * g + t];
-            v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
-          }
-          if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+        for (int t = 0; t < 4; ++t) {
+          v0[t] = acc[0][i][j][4 * g + t];
+          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
         }
-    }
+        if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+      });
+    });
   } else {
     // direct 32x32 result: lane holds column (lane % 32), rows 8 (v/4) + 4 (lane/32) + v%4
 #pragma unroll
@@ -745,27 +759,23 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // With the B fragment as the MFMA's first operand the 32x32 result is
   // transposed: lane l holds row (l % 32) of the block and, for v = 4g + t,
   // column 8 g + 4 (l / 32) + t, i.e. four consecutive columns per g.
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  StaticFor<0, MI>::run([&](auto i_tag) {
+    constexpr int i = decltype(i_tag)::value;
     const int r = wm * WM + i * 32 + (lane & 31);
     const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
-    if (!row_ok) continue;
     const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
+    StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
+      constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
+      const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+      float v0[4], v1[4];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        if (c >= p.N) continue;
-        float v0[4], v1[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v0[t] = acc[0][i][j][4 * g + t];
-          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
-        }
-        epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+      for (int t = 0; t < 4; ++t) {
+        v0[t] = acc[0][i][j][4 * g + t];
+        v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
       }
-  }
+      if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+    });
+  });
 #endif
 }
 
@@ -876,10 +886,10 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   if (bf16) {
     constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
-    if constexpr (kUseW4 && !KGROUP && EPI != EPI_SWIGLU_BWD) {
+    if constexpr (kUseW4 && !KGROUP) {
       // the one-wavefront-per-SIMD form for the M-grouped products; the
-      // weight gradients and the SwiGLU-backward product keep the eight-
-      // wavefront form (their extra live registers do not fit one SIMD's file
+      // weight gradients keep the eight-wavefront form (their address state
+      // for two transposed operands does not fit one SIMD's register file
       // next to 256 accumulators)
       auto kern = gemm_bf16_w4_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads4), 0, s, p);

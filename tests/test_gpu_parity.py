@@ -89,6 +89,8 @@ CASES = [
     # (id, config, overrides): reduced sizes span several tiles and ragged tails
     ("c1_tiny_fp32", "c1", {}),
     ("c2_mixtral_shape_small", "c2", dict(S=300, H=256, Hf=384)),
+    # ~500 rows per expert: two M tiles each, the second ragged
+    ("c2_mixtral_shape_multi_tile", "c2", dict(S=2000, H=256, Hf=384)),
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
