@@ -43,7 +43,9 @@ def kernel_model(name, cfg, counts):
         "bwd_dW2": (2 * R * Hf * H, Gb + R * H * b + R * Hf * b),
         "bwd_dxd": (4 * R * H * Hf, 2 * Wb + 2 * R * Hf * b + R * H * b),
         "bwd_dW13": (4 * R * H * Hf, 2 * Gb + R * H * b + 2 * R * Hf * b),
-        "dispatch_bwd_dx": (2 * R * H, R * H * b + S * H * b + R * H * b),
+        # the K router-weight rows each token gathers come from the small
+        # cached [E, H] table: counted once
+        "dispatch_bwd_dx": (2 * R * H, R * H * b + S * H * b + E * H * b + 8 * S * K),
         "router_dWg_partial": (2 * R * H, R * H * b + 4 * R),
     }
     return m.get(name)

@@ -22,12 +22,55 @@
 
 namespace moe {
 
+// Rows are read as 16-byte pieces (8 bf16 or 4 fp32 values) through one
+// buffer descriptor per (token, k) held in scalar registers; a pair with no
+// row (k >= K, or an invalid row index) gets an empty range and reads zero,
+// and pieces past the row end read zero too, so the loads carry no branches
+// and all K of them (for two or four column chunks) are in flight at once.
 template <bool BF16>
+struct Piece {
+  static constexpr int kEl = BF16 ? 8 : 4;   // values per 16-byte piece
+  static constexpr int kEb = BF16 ? 2 : 4;   // bytes per value
+  __device__ __forceinline__ static void unpack(const u32x4 w, float (&v)[8]) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+    }
+  }
+  __device__ __forceinline__ static u32x4 pack(const float (&v)[8]) {
+    u32x4 w;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+    }
+    return w;
+  }
+};
+
+// Descriptor of row `row` (wave-uniform) of a [rows, H] tensor; empty when !ok.
+template <bool BF16>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int row, int H,
+                                                           bool ok) {
+  const int r = __builtin_amdgcn_readfirstlane(ok ? row : 0);
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)H * Piece<BF16>::kEb : 0u);
+  return make_rsrc(reinterpret_cast<const char*>(base) + (int64_t)r * H * Piece<BF16>::kEb, bytes);
+}
+
+constexpr int kCombU = 2;  // column chunks (of 64 pieces) per iteration
+
+template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gates,
                                                       void* __restrict__ out, int S, int H, int K,
                                                       int64_t R) {
+  using PC = Piece<BF16>;
   const int lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= S) return;
@@ -38,47 +81,73 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     if (rk < 0 || rk >= R) rk = -1;
     gk = gates[(int64_t)s * K + lane];
   }
-  int rows[16];
-  float g[16];
+  __amdgpu_buffer_rsrc_t rs[KT];
+  float g[KT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    rows[k] = __shfl(rk, k < K ? k : 0, kWave);
-    g[k] = __shfl(gk, k < K ? k : 0, kWave);
+  for (int k = 0; k < KT; ++k) {
+    const int r = __shfl(rk, k < K ? k : 0, kWave);
+    g[k] = k < K ? __shfl(gk, k, kWave) : 0.f;
+    rs[k] = row_rsrc<BF16>(y, r, H, k < K && r >= 0);
   }
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int pieces = H / PC::kEl;
+  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
+    u32x4 w[kCombU][KT];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < K && rows[k] >= 0) {
+    for (int u = 0; u < kCombU; ++u)
+#pragma unroll
+      for (int k = 0; k < KT; ++k) w[u][k] = buf_load16(rs[k], (uint32_t)(p0 + 64 * u) * 16u);
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+      const int p = p0 + 64 * u;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {  // k order: the gates' order
         float v[8];
-        load8<BF16>(y, (int64_t)rows[k] * H + c, v);
+        PC::unpack(w[u][k], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += g[k] * v[i];
+        for (int i = 0; i < PC::kEl; ++i) acc[i] += g[k] * v[i];
       }
+      if (p < pieces)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
+                                  ((int64_t)s * H + (int64_t)p * PC::kEl) * PC::kEb) = PC::pack(acc);
     }
-    store8<BF16>(out, (int64_t)s * H + c, acc);
   }
 }
+
+// K rounded up to a power of two (1..16) as a compile-time bound
+template <template <bool, int> class Launch, bool BF16, typename... A>
+static void with_kt(int K, A... args) {
+  if (K <= 1) Launch<BF16, 1>::run(args...);
+  else if (K <= 2) Launch<BF16, 2>::run(args...);
+  else if (K <= 4) Launch<BF16, 4>::run(args...);
+  else if (K <= 8) Launch<BF16, 8>::run(args...);
+  else Launch<BF16, 16>::run(args...);
+}
+
+template <bool BF16, int KT>
+struct CombineLaunch {
+  static void run(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
+                  int H, int K, int64_t R, hipStream_t s) {
+    hipLaunchKernelGGL((combine_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0, s,
+                       y, row_of, gates, out, (int)S, H, K, R);
+  }
+};
 
 void launch_combine(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
                     int H, int K, int64_t R, bool bf16, hipStream_t s) {
   if (S <= 0) return;
   TimedLaunch tl("combine", s);
-  const int blocks = (int)((S + 3) / 4);
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, y, row_of, gates, out,
-                       (int)S, H, K, R);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, y, row_of, gates, out,
-                       (int)S, H, K, R);
+  if (bf16) with_kt<CombineLaunch, true>(K, y, row_of, gates, out, S, H, K, R, s);
+  else with_kt<CombineLaunch, false>(K, y, row_of, gates, out, S, H, K, R, s);
 }
 
-template <bool BF16>
+template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const void* __restrict__ dout, const void* __restrict__ y, const int32_t* __restrict__ row_of,
     const int32_t* __restrict__ idx, const float* __restrict__ gates, void* __restrict__ dy,
     float* __restrict__ dgates, float* __restrict__ dlogits, float* __restrict__ dl_row, int S,
     int H, int E, int K, int64_t R) {
+  using PC = Piece<BF16>;
   const int lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= S) return;
@@ -90,34 +159,50 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     ek = idx[(int64_t)s * K + lane];
     gk = gates[(int64_t)s * K + lane];
   }
-  int rows[16];
-  float g[16], dot[16];
+  __amdgpu_buffer_rsrc_t rs[KT];
+  int rows[KT];
+  float g[KT], dot[KT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    rows[k] = __shfl(rk, k < K ? k : 0, kWave);
-    g[k] = __shfl(gk, k < K ? k : 0, kWave);
+  for (int k = 0; k < KT; ++k) {
+    rows[k] = k < K ? __shfl(rk, k, kWave) : -1;
+    g[k] = k < K ? __shfl(gk, k, kWave) : 0.f;
     dot[k] = 0.f;
+    rs[k] = row_rsrc<BF16>(y, rows[k], H, rows[k] >= 0);
   }
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    float d[8];
-    load8<BF16>(dout, (int64_t)s * H + c, d);
+  const __amdgpu_buffer_rsrc_t rd = row_rsrc<BF16>(dout, s, H, true);
+  const int pieces = H / PC::kEl;
+  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
+    u32x4 wd[kCombU], w[kCombU][KT];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < K && rows[k] >= 0) {
+    for (int u = 0; u < kCombU; ++u) {
+      wd[u] = buf_load16(rd, (uint32_t)(p0 + 64 * u) * 16u);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) w[u][k] = buf_load16(rs[k], (uint32_t)(p0 + 64 * u) * 16u);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+      const int p = p0 + 64 * u;
+      float d[8];
+      PC::unpack(wd[u], d);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
         float v[8], o[8];
-        load8<BF16>(y, (int64_t)rows[k] * H + c, v);
+        PC::unpack(w[u][k], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < PC::kEl; ++i) {
           dot[k] += d[i] * v[i];
           o[i] = g[k] * d[i];
         }
-        store8<BF16>(dy, (int64_t)rows[k] * H + c, o);
+        if (rows[k] >= 0 && p < pieces)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dy) +
+                                    ((int64_t)rows[k] * H + (int64_t)p * PC::kEl) * PC::kEb) =
+              PC::pack(o);
       }
     }
   }
   float my_dg = 0.f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < KT; ++k) {
     if (k < K) {
       const float t = wave_sum(dot[k]);
       if (lane == k) my_dg = t;
@@ -131,21 +216,32 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     if (rk >= 0) dl_row[rk] = my_dl;
   }
   // Dense logit-gradient row: zero off the chosen experts.
-  int ee[16];
-  float dd[16];
+  int ee[KT];
+  float dd[KT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    ee[k] = __shfl(ek, k < K ? k : 0, kWave);
+  for (int k = 0; k < KT; ++k) {
+    ee[k] = k < K ? __shfl(ek, k, kWave) : -1;
     dd[k] = __shfl(my_dl, k < K ? k : 0, kWave);
   }
   for (int e = lane; e < E; e += 64) {
     float v = 0.f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k < K && ee[k] == e) v = dd[k];
+    for (int k = 0; k < KT; ++k)
+      if (ee[k] == e) v = dd[k];
     dlogits[(int64_t)s * E + e] = v;
   }
 }
+
+template <bool BF16, int KT>
+struct CombineBwdLaunch {
+  static void run(const void* dout, const void* y, const int32_t* row_of, const int32_t* idx,
+                  const float* gates, void* dy, float* dgates, float* dlogits, float* dl_row,
+                  int64_t S, int H, int E, int K, int64_t R, hipStream_t s) {
+    hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0,
+                       s, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E,
+                       K, R);
+  }
+};
 
 void launch_combine_bwd(const void* dout, const void* y, const int32_t* row_of,
                         const int32_t* idx, const float* gates, void* dy, float* dgates,
@@ -153,16 +249,15 @@ void launch_combine_bwd(const void* dout, const void* y, const int32_t* row_of,
                         bool bf16, hipStream_t s) {
   if (S <= 0) return;
   TimedLaunch tl("combine_bwd", s);
-  const int blocks = (int)((S + 3) / 4);
   if (bf16)
-    hipLaunchKernelGGL(combine_bwd_kernel<true>, dim3(blocks), dim3(256), 0, s, dout, y, row_of,
-                       idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E, K, R);
+    with_kt<CombineBwdLaunch, true>(K, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, S,
+                                    H, E, K, R, s);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<false>, dim3(blocks), dim3(256), 0, s, dout, y, row_of,
-                       idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E, K, R);
+    with_kt<CombineBwdLaunch, false>(K, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row,
+                                     S, H, E, K, R, s);
 }
 
-template <bool BF16>
+template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dxd,
                                                  const int32_t* __restrict__ row_of,
                                                  const int32_t* __restrict__ idx,
@@ -170,6 +265,7 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dxd,
                                                  const void* __restrict__ wgT,
                                                  void* __restrict__ dx, int S, int H, int E, int K,
                                                  int64_t R) {
+  using PC = Piece<BF16>;
   const int lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= S) return;
@@ -182,50 +278,68 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dxd,
     if (ek < 0 || ek >= E) ek = -1;
     else dk = dlogits[(int64_t)s * E + ek];
   }
-  int rows[16], ex[16];
-  float dl[16];
+  __amdgpu_buffer_rsrc_t rr[KT], re[KT];
+  float dl[KT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    rows[k] = __shfl(rk, k < K ? k : 0, kWave);
-    ex[k] = __shfl(ek, k < K ? k : 0, kWave);
-    dl[k] = __shfl(dk, k < K ? k : 0, kWave);
+  for (int k = 0; k < KT; ++k) {
+    const int r = k < K ? __shfl(rk, k, kWave) : -1;
+    const int ex = k < K ? __shfl(ek, k, kWave) : -1;
+    dl[k] = k < K ? __shfl(dk, k, kWave) : 0.f;
+    rr[k] = row_rsrc<BF16>(dxd, r, H, r >= 0);
+    re[k] = row_rsrc<BF16>(wgT, ex, H, ex >= 0);
   }
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int pieces = H / PC::kEl;
+  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
+    u32x4 wr[kCombU][KT], we[kCombU][KT];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < K && rows[k] >= 0) {
-        float v[8];
-        load8<BF16>(dxd, (int64_t)rows[k] * H + c, v);
+    for (int u = 0; u < kCombU; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int k = 0; k < KT; ++k) {
+        wr[u][k] = buf_load16(rr[k], (uint32_t)(p0 + 64 * u) * 16u);
+        we[u][k] = buf_load16(re[k], (uint32_t)(p0 + 64 * u) * 16u);
       }
-    }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < K && ex[k] >= 0) {
+    for (int u = 0; u < kCombU; ++u) {
+      const int p = p0 + 64 * u;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {  // the K dispatched rows, in k order
         float v[8];
-        load8<BF16>(wgT, (int64_t)ex[k] * H + c, v);
+        PC::unpack(wr[u][k], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += dl[k] * v[i];
+        for (int i = 0; i < PC::kEl; ++i) acc[i] += v[i];
       }
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {  // then the router term, in k order
+        float v[8];
+        PC::unpack(we[u][k], v);
+#pragma unroll
+        for (int i = 0; i < PC::kEl; ++i) acc[i] += dl[k] * v[i];
+      }
+      if (p < pieces)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dx) +
+                                  ((int64_t)s * H + (int64_t)p * PC::kEl) * PC::kEb) = PC::pack(acc);
     }
-    store8<BF16>(dx, (int64_t)s * H + c, acc);
   }
 }
+
+template <bool BF16, int KT>
+struct DxLaunch {
+  static void run(const void* dxd, const int32_t* row_of, const int32_t* idx, const float* dlogits,
+                  const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R,
+                  hipStream_t s) {
+    hipLaunchKernelGGL((dx_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0, s, dxd,
+                       row_of, idx, dlogits, wgT, dx, (int)S, H, E, K, R);
+  }
+};
 
 void launch_dx(const void* dxd, const int32_t* row_of, const int32_t* idx, const float* dlogits,
                const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R, bool bf16,
                hipStream_t s) {
   if (S <= 0) return;
   TimedLaunch tl("dispatch_bwd_dx", s);
-  const int blocks = (int)((S + 3) / 4);
-  if (bf16)
-    hipLaunchKernelGGL(dx_kernel<true>, dim3(blocks), dim3(256), 0, s, dxd, row_of, idx, dlogits,
-                       wgT, dx, (int)S, H, E, K, R);
-  else
-    hipLaunchKernelGGL(dx_kernel<false>, dim3(blocks), dim3(256), 0, s, dxd, row_of, idx, dlogits,
-                       wgT, dx, (int)S, H, E, K, R);
+  if (bf16) with_kt<DxLaunch, true>(K, dxd, row_of, idx, dlogits, wgT, dx, S, H, E, K, R, s);
+  else with_kt<DxLaunch, false>(K, dxd, row_of, idx, dlogits, wgT, dx, S, H, E, K, R, s);
 }
 
 // Router-weight gradient, balanced over skewed experts.  Each expert's rows

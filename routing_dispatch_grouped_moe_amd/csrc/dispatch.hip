@@ -121,18 +121,26 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   int rows[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) rows[k] = __shfl(row, k < K ? k : 0, kWave);
+  // four 16-byte pieces per lane in flight per iteration (the token's row is
+  // read once, through a descriptor so pieces past the row end read zero)
   constexpr int kEl = BF16 ? 8 : 4;  // elements per 16-byte piece
+  constexpr int kU = 4;
   const int pieces = H / kEl;
-  const u32x4* src = reinterpret_cast<const u32x4*>(
-      reinterpret_cast<const char*>(x) + (int64_t)s * H * (BF16 ? 2 : 4));
-  for (int c = lane; c < pieces; c += 64) {
-    const u32x4 v = src[c];
+  const uint32_t row_bytes = (uint32_t)H * (BF16 ? 2u : 4u);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(reinterpret_cast<const char*>(x) + (int64_t)s * row_bytes, row_bytes);
+  for (int c0 = lane; c0 < pieces; c0 += 64 * kU) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = buf_load16(rx, (uint32_t)(c0 + 64 * u) * 16u);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (k < K && rows[k] >= 0) {
         u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(xd) +
-                                              (int64_t)rows[k] * H * (BF16 ? 2 : 4));
-        dst[c] = v;
+                                              (int64_t)rows[k] * row_bytes);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (c0 + 64 * u < pieces) dst[c0 + 64 * u] = v[u];
       }
     }
   }

@@ -249,6 +249,30 @@ __device__ __forceinline__ u32x4 frag_km(const char* tile, int col_base, int kk,
   }
   return r;
 }
+// The swizzle term of km_off depends on k only through k & 3 and
+// (k >> 3) & 1, which for the rows a lane reads are fixed by the lane; so a
+// fragment's two transpose loads for any K16 slice kk are at
+// base + kk * 16 rows + h * 4 rows, with one per-lane base per fragment.
+template <int COLS>
+__device__ __forceinline__ uint32_t frag_km_base(int col_base, int lane) {
+  return km_off<COLS>(8 * (lane >> 5) + ((lane & 15) >> 2),
+                      (col_base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3) +
+         (4 * (lane & 3) & 7) * 2;
+}
+template <int COLS>
+__device__ __forceinline__ u32x4 frag_km_at(const char* tile, uint32_t base, int kk) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t off = base + (uint32_t)(16 * kk + 4 * h) * (COLS * 2);
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)((__attribute__((address_space(3))) char*)(tile) + off));
+    const u32x2 u = __builtin_bit_cast(u32x2, v);
+    r[2 * h] = u[0];
+    r[2 * h + 1] = u[1];
+  }
+  return r;
+}
 
 // One operand tile of one K step, staged global -> registers -> LDS.
 //   KC:  stored [rows][K] in HBM, tile rows [0, ROWS), k [k0, k0+64)
@@ -667,15 +691,21 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
 
   u32x4 af0[MI], bf0[NB][NJ], af1[MI], bf1[NB][NJ];
   // fragment f of slice kk: f < MI an A fragment, else B fragment (q, j)
+  // per-lane LDS bases of the transposed fragments (loop invariant)
+  uint32_t abase[MI], bbase[NJ];
+#pragma unroll
+  for (int f = 0; f < MI; ++f) abase[f] = frag_km_base<BM>(wm * WM + f * 32, lane);
+#pragma unroll
+  for (int f = 0; f < NJ; ++f) bbase[f] = frag_km_base<BN>(wn * WN + f * 32, lane);
   auto read_frag = [&](const char* st, int kk, int f, u32x4 (&af)[MI], u32x4 (&bfr)[NB][NJ]) {
     if (f < MI) {
       if constexpr (A_KC) af[f] = frag_kc(st, wm * WM + f * 32, kk, lane);
-      else af[f] = frag_km<BM>(st, wm * WM + f * 32, kk, lane);
+      else af[f] = frag_km_at<BM>(st, abase[f], kk);
     } else {
       const int q = (f - MI) / NJ, j = (f - MI) % NJ;
       const char* t = st + kTileA + q * kTileB;
       if constexpr (B_KC) bfr[q][j] = frag_kc(t, wn * WN + j * 32, kk, lane);
-      else bfr[q][j] = frag_km<BN>(t, wn * WN + j * 32, kk, lane);
+      else bfr[q][j] = frag_km_at<BN>(t, bbase[j], kk);
     }
   };
   constexpr int kMfma = MI * NB * NJ;
