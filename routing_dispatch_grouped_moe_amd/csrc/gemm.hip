@@ -60,7 +60,10 @@ constexpr int kBK = 64;
 constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
 constexpr int kGroupM = 4;  // M tiles walked together (n fastest inside the group)
 
-enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
+// EPI_F32 overwrites the fp32 weight gradient, EPI_F32_ACC adds to it (two
+// kinds, so the overwrite form carries no loads of the old values)
+enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3, EPI_F32_ACC = 4 };
+constexpr bool epi_f32(int epi) { return epi == EPI_F32 || epi == EPI_F32_ACC; }
 
 struct GemmArgs {
   const int32_t* cu;      // [E+1] row offsets of the experts
@@ -105,10 +108,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
     // weight gradients are written once and not read again in the layer:
     // non-temporal stores keep them from displacing operand tiles in L2
     float* c0 = reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + o;
-    __builtin_nontemporal_store(p.accum ? *c0 + v0 : v0, c0);
+    __builtin_nontemporal_store(EPI == EPI_F32_ACC ? *c0 + v0 : v0, c0);
     if constexpr (DUAL) {
       float* c1 = reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o;
-      __builtin_nontemporal_store(p.accum ? *c1 + v1 : v1, c1);
+      __builtin_nontemporal_store(EPI == EPI_F32_ACC ? *c1 + v1 : v1, c1);
     }
   }
 }
@@ -143,12 +146,12 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& p, int e, int64_t row,
   } else {
     float4* c0 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + o);
     float4 w0 = make_float4(v0[0], v0[1], v0[2], v0[3]);
-    if (p.accum) { const float4 q = *c0; w0.x += q.x; w0.y += q.y; w0.z += q.z; w0.w += q.w; }
+    if (EPI == EPI_F32_ACC) { const float4 q = *c0; w0.x += q.x; w0.y += q.y; w0.z += q.z; w0.w += q.w; }
     *c0 = w0;
     if constexpr (DUAL) {
       float4* c1 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o);
       float4 w1 = make_float4(v1[0], v1[1], v1[2], v1[3]);
-      if (p.accum) { const float4 q = *c1; w1.x += q.x; w1.y += q.y; w1.z += q.z; w1.w += q.w; }
+      if (EPI == EPI_F32_ACC) { const float4 q = *c1; w1.x += q.x; w1.y += q.y; w1.z += q.z; w1.w += q.w; }
       *c1 = w1;
     }
   }
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   // where each 4-byte store instruction writes two whole 128-byte rows,
   // which suits these write-bound products better than 16-byte pieces
   // scattered over 32 rows
-  constexpr bool kSwapAB = EPI != EPI_F32;
+  constexpr bool kSwapAB = !epi_f32(EPI);
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   if constexpr (KGROUP) {
     // A: [rows][M] of expert e (A^T read), B: [rows][N]; the reduction runs over the rows.
     if (valid == 0) {
-      if (!p.accum) {
+      if (EPI != EPI_F32_ACC) {
         for (int i = tid; i < BM * BN; i += kThreads) {
           const int r = i / BN, c = i % BN;
           if (m0 + r < p.M && n0 + c < p.N) epilogue<EPI, true, DUAL>(p, e, m0 + r, n0 + c, 0.f, 0.f);
@@ -605,6 +608,9 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
+  // bf16 outputs take the transposed MFMA result (8-byte output pieces); the
+  // fp32 weight gradients keep the direct one (whole-row 4-byte stores)
+  constexpr bool kSwapAB = !epi_f32(EPI);
   // one LDS object per stage: the compiler can then tell that direct loads
   // into one stage never alias fragment reads of the other, and does not make
   // those reads wait for the loads
@@ -626,7 +632,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   const int nk_seg = KGROUP ? 0 : p.K / kBK;
   if constexpr (KGROUP) {
     if (valid == 0) {
-      if (!p.accum) {
+      if (EPI != EPI_F32_ACC) {
         for (int i = tid; i < BM * BN; i += kThreads4) {
           const int r = i / BN, c = i % BN;
           if (m0 + r < p.M && n0 + c < p.N) epilogue<EPI, true, DUAL>(p, e, m0 + r, n0 + c, 0.f, 0.f);
@@ -727,9 +733,13 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
 #pragma unroll
     for (int t = 0; t < kMfma; ++t) {
       const int i = t / (NB * NJ), q = (t / NJ) % NB, j = t % NJ;
-      acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, bfc[q][j]), __builtin_bit_cast(bf16x8, afc[i]), acc[q][i][j],
-          0, 0, 0);
+      acc[q][i][j] = kSwapAB
+          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfc[q][j]),
+                                                    __builtin_bit_cast(bf16x8, afc[i]), acc[q][i][j],
+                                                    0, 0, 0)
+          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, afc[i]),
+                                                    __builtin_bit_cast(bf16x8, bfc[q][j]),
+                                                    acc[q][i][j], 0, 0, 0);
       if (rd != nullptr && t < kFrag) read_frag(rd, rd_kk, t, afn, bfn);
       if constexpr (DMA)
         if (t % (kMfma / kHalf) == 0) issue_one(d0 + t / (kMfma / kHalf), ra, rb, ds);
@@ -789,23 +799,43 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // With the B fragment as the MFMA's first operand the 32x32 result is
   // transposed: lane l holds row (l % 32) of the block and, for v = 4g + t,
   // column 8 g + 4 (l / 32) + t, i.e. four consecutive columns per g.
-  StaticFor<0, MI>::run([&](auto i_tag) {
-    constexpr int i = decltype(i_tag)::value;
-    const int r = wm * WM + i * 32 + (lane & 31);
-    const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
-    const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
-    StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
-      constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
-      const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-      float v0[4], v1[4];
+  if constexpr (kSwapAB) {
+    StaticFor<0, MI>::run([&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value;
+      const int r = wm * WM + i * 32 + (lane & 31);
+      const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
+      const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
+      StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
+        constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
+        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        float v0[4], v1[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v0[t] = acc[0][i][j][4 * g + t];
-        v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
-      }
-      if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+        for (int t = 0; t < 4; ++t) {
+          v0[t] = acc[0][i][j][4 * g + t];
+          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
+        }
+        if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+      });
     });
-  });
+  } else {
+    // direct 32x32 result: lane holds column (lane % 32), rows 8 (v/4) + 4 (lane/32) + v%4
+    StaticFor<0, MI * NJ>::run([&](auto ij_tag) {
+      constexpr int i = decltype(ij_tag)::value / NJ, j = decltype(ij_tag)::value % NJ;
+      const int c = n0 + wn * WN + j * 32 + (lane & 31);
+      if (c < p.N) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
+          if constexpr (KGROUP) {
+            if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
+          } else {
+            if (r < valid) epilogue<EPI, true, DUAL>(p, e, row0 + r, c, acc[0][i][j][v], v1);
+          }
+        }
+      }
+    });
+  }
 #endif
 }
 
@@ -838,7 +868,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         acc0 = fmaf(a, B0[gr * p.ldb + col], acc0);
         if constexpr (DUAL) acc1 = fmaf(a, B1[gr * p.ldb + col], acc1);
       }
-      if (valid > 0 || !p.accum) epilogue<EPI, false, DUAL>(p, e, m0 + r, col, acc0, acc1);
+      if (valid > 0 || EPI != EPI_F32_ACC) epilogue<EPI, false, DUAL>(p, e, m0 + r, col, acc0, acc1);
     } else {
       if (r >= valid) continue;
       const int64_t gr = row0 + r;
@@ -897,8 +927,8 @@ void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hi
 }
 
 // -------------------------------------------------------------- launches --
-constexpr bool kUseW4 = true;
-template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
+template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI,
+          bool W4 = true>
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
   static_assert(KGROUP || BM == kGemmBM, "M-grouped tiles follow the tile table");
   const int bm = bf16 ? BM : kBMf, bn = bf16 ? BN : kBNf;
@@ -916,11 +946,10 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   if (bf16) {
     constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
-    if constexpr (kUseW4 && !KGROUP) {
-      // the one-wavefront-per-SIMD form for the M-grouped products; the
-      // weight gradients keep the eight-wavefront form (their address state
-      // for two transposed operands does not fit one SIMD's register file
-      // next to 256 accumulators)
+    if constexpr (W4 && EPI != EPI_F32_ACC) {
+      // the one-wavefront-per-SIMD form; accumulating weight gradients keep
+      // the eight-wavefront form (the old values they load do not fit one
+      // SIMD's register file next to 256 accumulators)
       auto kern = gemm_bf16_w4_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads4), 0, s, p);
     } else {
@@ -937,6 +966,13 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
                        dim3(256), 0, s, p);
   }
 }
+
+// The weight-gradient products reduce over each expert's rows.  With many
+// rows per expert (mean at least 1024) they run long K loops and take the
+// one-wavefront-per-SIMD form; with few, the K loop is a handful of steps
+// and the eight-wavefront form (no even-step rounding, shorter per-tile
+// set-up) is faster.  The host knows the mean without reading the counts.
+static bool many_rows(int64_t R, int E) { return R >= (int64_t)1024 * E; }
 
 static GemmArgs base_args(const int32_t* cu, const WsLayout& L, char* ws, int E) {
   GemmArgs p{};
@@ -1005,7 +1041,6 @@ void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const v
 
 void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,
                     int Hf, int E, bool accum, bool bf16, hipStream_t s) {
-  (void)R;
   // dW2[e][Hf, H] = a[rows, Hf]^T * dy[rows, H]
   GemmArgs p{};
   p.cu = cu; p.E = E; p.M = Hf; p.N = H;
@@ -1013,13 +1048,18 @@ void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2
   p.B0 = dy; p.ldb = H;
   p.C0 = dW2; p.ldc = H; p.sCe = (int64_t)Hf * H;
   p.accum = accum;
-  gemm_launch<256, 256, false, false, false, false, true, EPI_F32>("bwd_dW2", p, 0, bf16, s);
+  if (accum)
+    gemm_launch<256, 256, false, false, false, false, true, EPI_F32_ACC, false>("bwd_dW2", p, 0,
+                                                                                bf16, s);
+  else if (many_rows(R, E))
+    gemm_launch<256, 256, false, false, false, false, true, EPI_F32, true>("bwd_dW2", p, 0, bf16, s);
+  else
+    gemm_launch<256, 256, false, false, false, false, true, EPI_F32, false>("bwd_dW2", p, 0, bf16, s);
 }
 
 void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int32_t* cu,
                      float* dW1, float* dW3, int64_t R, int H, int Hf, int E, bool accum,
                      bool bf16, hipStream_t s) {
-  (void)R;
   // dW1[e][H, Hf] = xd[rows, H]^T * dh1[rows, Hf]; dW3 likewise with dh3.
   GemmArgs p{};
   p.cu = cu; p.E = E; p.M = H; p.N = Hf;
@@ -1027,7 +1067,13 @@ void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int
   p.B0 = dh1; p.B1 = dh3; p.ldb = Hf;
   p.C0 = dW1; p.C1 = dW3; p.ldc = Hf; p.sCe = (int64_t)H * Hf;
   p.accum = accum;
-  gemm_launch<256, 128, false, false, true, false, true, EPI_F32>("bwd_dW13", p, 0, bf16, s);
+  if (accum)
+    gemm_launch<256, 128, false, false, true, false, true, EPI_F32_ACC, false>("bwd_dW13", p, 0,
+                                                                               bf16, s);
+  else if (many_rows(R, E))
+    gemm_launch<256, 128, false, false, true, false, true, EPI_F32, true>("bwd_dW13", p, 0, bf16, s);
+  else
+    gemm_launch<256, 128, false, false, true, false, true, EPI_F32, false>("bwd_dW13", p, 0, bf16, s);
 }
 
 }  // namespace moe

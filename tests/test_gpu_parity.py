@@ -89,8 +89,10 @@ CASES = [
     # (id, config, overrides): reduced sizes span several tiles and ragged tails
     ("c1_tiny_fp32", "c1", {}),
     ("c2_mixtral_shape_small", "c2", dict(S=300, H=256, Hf=384)),
-    # ~500 rows per expert: two M tiles each, the second ragged
-    ("c2_mixtral_shape_multi_tile", "c2", dict(S=2000, H=256, Hf=384)),
+    # 525 rows per expert: three M tiles each, the last ragged; above the
+    # few-rows bound of the weight-gradient products (smaller shares use the
+    # small-tile form)
+    ("c2_mixtral_shape_multi_tile", "c2", dict(S=2100, H=256, Hf=384)),
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
@@ -187,3 +189,47 @@ def test_zero_tokens():
     torch.cuda.synchronize()
     assert not to_host(layer.counts).any() and not to_host(layer.cu).any()
     assert not to_host(layer.dW1).any() and not to_host(layer.dWg).any()
+
+
+@pytest.mark.parametrize("cid,cfg,ov", [
+    ("c3_zipf_small_accum", "c3", dict(S=257, H=256, Hf=256)),
+    ("c2_multi_tile_accum", "c2", dict(S=2100, H=256, Hf=384, E=12)),
+], ids=["c3_zipf_small_accum", "c2_multi_tile_accum"])
+def test_accumulated_weight_gradients(cid, cfg, ov):
+    """MOE_F_ACCUM_GRAD adds the step's weight gradients to what the buffers hold.
+
+    The buffers are prefilled with a known pattern P; afterwards dW - P must
+    match the oracle's gradient to the bf16 tolerance, and an expert with no
+    rows must still hold exactly P.
+    """
+    _say(f"[accum] {cid} {ov}")
+    wl = make_workload(cfg, **ov, host_weights=True)
+    # expert E-1 gets no rows: every token's bias for it is very negative
+    bias = np.zeros(wl.E, np.float32) if wl.bias is None else wl.bias.copy()
+    bias[wl.E - 1] = -1e4
+    wl.bias = bias
+    dt = wl.dtype
+    x, Wg = to_dev(wl.x, dt), to_dev(wl.Wg, dt)
+    W1, W3, W2, dout = to_dev(wl.W1, dt), to_dev(wl.W3, dt), to_dev(wl.W2, dt), to_dev(wl.dout, dt)
+    b = torch.from_numpy(bias).cuda()
+    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt, flags=L.MOE_F_RENORM | L.MOE_F_ACCUM_GRAD)
+    pats = {}
+    for n in ("dW1", "dW3", "dW2", "dWg"):
+        g = getattr(layer, n)
+        pat = torch.linspace(-0.5, 0.5, g.numel(), dtype=torch.float32, device="cuda").view_as(g)
+        g.copy_(pat)
+        pats[n] = to_host(pat)
+    layer.forward(x, Wg, b, W1, W3, W2)
+    layer.backward(dout, x, Wg, W1, W3, W2)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    counts = to_host(layer.counts)
+    assert counts[wl.E - 1] == 0
+    _, bw = oracle_on_gpu_routing(wl.x, wl.Wg, bias, wl.W1, wl.W3, wl.W2, wl.K,
+                                  to_host(layer.logits), wl.dout)
+    for n in ("dW1", "dW3", "dW2", "dWg"):
+        got = to_host(getattr(layer, n)).astype(np.float64) - pats[n]
+        assert_close(f"{n} increment", got, bw[n], BF16_TOL)
+    for n in ("dW1", "dW3", "dW2"):
+        np.testing.assert_array_equal(to_host(getattr(layer, n))[wl.E - 1], pats[n][wl.E - 1],
+                                      err_msg=f"{n}: an expert without rows must keep its values")
