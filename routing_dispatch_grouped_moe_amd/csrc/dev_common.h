@@ -19,16 +19,15 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> two bf16 in one word (lo in bits 0..15), round to nearest even,
+// NaN stays NaN: one gfx950 v_cvt_pk_bf16_f32 per pair.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2_v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // Load / store 8 consecutive elements as fp32, from bf16 or fp32 storage.
 template <bool BF16>
@@ -119,7 +118,15 @@ __device__ __forceinline__ uint64_t topk_key(float logit, int e) {
 }
 __device__ __forceinline__ int key_expert(uint64_t key) { return int(~uint32_t(key)); }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+// Logistic sigmoid from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each, far below the bf16 rounding of
+// every SwiGLU output): e^-z = 2^(-z log2 e).  Both ends saturate exactly:
+// z -> -inf gives rcp(inf) = 0, z -> +inf gives rcp(1) = 1.  Four
+// instructions instead of a range-reduced expf and an IEEE division, which
+// matters in GEMM epilogues that evaluate it for every output element.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 }  // namespace moe

@@ -799,7 +799,59 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // With the B fragment as the MFMA's first operand the 32x32 result is
   // transposed: lane l holds row (l % 32) of the block and, for v = 4g + t,
   // column 8 g + 4 (l / 32) + t, i.e. four consecutive columns per g.
-  if constexpr (kSwapAB) {
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    static_assert(kSwapAB && !KGROUP && !DUAL, "SwiGLU backward: M-grouped, one B operand");
+    // The epilogue reads h1 and h3.  Loaded piece by piece beside the stores,
+    // every piece waits a full memory round trip; instead the h1/h3 pieces of
+    // the next 32-row group are in flight while the current group is computed
+    // and stored.  The loads are unconditional (a piece outside the tile reads
+    // element 0) so they issue back to back; only the stores are masked.
+    constexpr int kP = NJ * 4;
+    u32x2 zb[2][kP], ub[2][kP];
+    const uint16_t* h1 = reinterpret_cast<const uint16_t*>(p.X0);
+    const uint16_t* h3 = reinterpret_cast<const uint16_t*>(p.X1);
+    auto load_group = [&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value, b = i & 1;
+      const int r = wm * WM + i * 32 + (lane & 31);
+      const bool row_ok = r < valid;
+      const int64_t ro = (row0 + r) * p.ldc;
+      StaticFor<0, kP>::run([&](auto jg_tag) {
+        constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
+        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        const int64_t o = (row_ok && c < p.N) ? ro + c : 0;
+        zb[b][jg] = *reinterpret_cast<const u32x2*>(h1 + o);
+        ub[b][jg] = *reinterpret_cast<const u32x2*>(h3 + o);
+      });
+    };
+    load_group(std::integral_constant<int, 0>{});
+    StaticFor<0, MI>::run([&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value, b = i & 1;
+      if constexpr (i + 1 < MI) load_group(std::integral_constant<int, i + 1>{});
+      const int r = wm * WM + i * 32 + (lane & 31);
+      const bool row_ok = r < valid;
+      const int64_t ro = (row0 + r) * p.ldc;
+      StaticFor<0, kP>::run([&](auto jg_tag) {
+        constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
+        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        const float z[4] = {bf16_lo(zb[b][jg][0]), bf16_hi(zb[b][jg][0]),
+                            bf16_lo(zb[b][jg][1]), bf16_hi(zb[b][jg][1])};
+        const float u[4] = {bf16_lo(ub[b][jg][0]), bf16_hi(ub[b][jg][0]),
+                            bf16_lo(ub[b][jg][1]), bf16_hi(ub[b][jg][1])};
+        float d1[4], d3[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = acc[0][i][j][4 * g + t];
+          const float sg = sigmoid_f(z[t]);
+          d1[t] = v * u[t] * sg * (1.0f + z[t] * (1.0f - sg));
+          d3[t] = v * z[t] * sg;
+        }
+        if (row_ok && c < p.N) {
+          store4_bf16(p.C0, ro + c, d1);
+          store4_bf16(p.C1, ro + c, d3);
+        }
+      });
+    });
+  } else if constexpr (kSwapAB) {
     StaticFor<0, MI>::run([&](auto i_tag) {
       constexpr int i = decltype(i_tag)::value;
       const int r = wm * WM + i * 32 + (lane & 31);
@@ -954,11 +1006,11 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads4), 0, s, p);
     } else {
       auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
-      if (!attr) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        attr = true;
-      }
+      // a failure stays the thread's last HIP error (so the entry point
+      // reports it) and the next call tries again
+      if (!attr)
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, s, p);
     }
   } else {
