@@ -608,9 +608,10 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
-  // bf16 outputs take the transposed MFMA result (8-byte output pieces); the
-  // fp32 weight gradients keep the direct one (whole-row 4-byte stores)
-  constexpr bool kSwapAB = !epi_f32(EPI);
+  // every output kind here leaves through the LDS-staged epilogue, which
+  // takes the transposed MFMA result (four consecutive columns per lane)
+  static_assert(EPI != EPI_F32_ACC, "accumulating weight gradients use the eight-wavefront form");
+  constexpr bool kSwapAB = true;
   // one LDS object per stage: the compiler can then tell that direct loads
   // into one stage never alias fragment reads of the other, and does not make
   // those reads wait for the loads
@@ -799,76 +800,217 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // With the B fragment as the MFMA's first operand the 32x32 result is
   // transposed: lane l holds row (l % 32) of the block and, for v = 4g + t,
   // column 8 g + 4 (l / 32) + t, i.e. four consecutive columns per g.
-  if constexpr (EPI == EPI_SWIGLU_BWD) {
-    static_assert(kSwapAB && !KGROUP && !DUAL, "SwiGLU backward: M-grouped, one B operand");
-    // The epilogue reads h1 and h3.  Loaded piece by piece beside the stores,
-    // every piece waits a full memory round trip; instead the h1/h3 pieces of
-    // the next 32-row group are in flight while the current group is computed
-    // and stored.  The loads are unconditional (a piece outside the tile reads
-    // element 0) so they issue back to back; only the stores are masked.
-    constexpr int kP = NJ * 4;
-    u32x2 zb[2][kP], ub[2][kP];
-    const uint16_t* h1 = reinterpret_cast<const uint16_t*>(p.X0);
-    const uint16_t* h3 = reinterpret_cast<const uint16_t*>(p.X1);
-    auto load_group = [&](auto i_tag) {
-      constexpr int i = decltype(i_tag)::value, b = i & 1;
-      const int r = wm * WM + i * 32 + (lane & 31);
-      const bool row_ok = r < valid;
-      const int64_t ro = (row0 + r) * p.ldc;
-      StaticFor<0, kP>::run([&](auto jg_tag) {
-        constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
-        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        const int64_t o = (row_ok && c < p.N) ? ro + c : 0;
-        zb[b][jg] = *reinterpret_cast<const u32x2*>(h1 + o);
-        ub[b][jg] = *reinterpret_cast<const u32x2*>(h3 + o);
-      });
+  // Written straight to memory, one such store instruction touches 32 rows
+  // with 16 bytes each; the bf16 outputs are instead staged through the two
+  // (now free) 64-KB LDS stages and leave as whole rows, 16 bytes a lane.
+  if constexpr (kSwapAB) {
+    static_assert(!KGROUP || EPI == EPI_F32, "staged epilogue kinds");
+    // every direct load has landed and every wavefront is done with the stages
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // A staged tile: rows of BN bf16 (RS bytes), 16-byte chunk c of row r at
+    // c ^ (r & 15).  A transposed piece write (32 rows, same chunk) then hits
+    // every bank group twice, and a row read hits each once per 16 chunks.
+    constexpr int RS = BN * 2, LPR = BN / 8, RPI = 64 / LPR;
+    auto put4 = [&](char* st, int r, int c, const float (&v)[4]) {
+      const uint32_t o = (uint32_t)r * RS + ((uint32_t)((c >> 3) ^ (r & 15)) << 4) + ((c >> 2) & 1) * 8;
+      u32x2 w2;
+      w2[0] = pack_bf16x2(v[0], v[1]);
+      w2[1] = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(st + o) = w2;
     };
-    load_group(std::integral_constant<int, 0>{});
-    StaticFor<0, MI>::run([&](auto i_tag) {
-      constexpr int i = decltype(i_tag)::value, b = i & 1;
-      if constexpr (i + 1 < MI) load_group(std::integral_constant<int, i + 1>{});
-      const int r = wm * WM + i * 32 + (lane & 31);
-      const bool row_ok = r < valid;
-      const int64_t ro = (row0 + r) * p.ldc;
-      StaticFor<0, kP>::run([&](auto jg_tag) {
-        constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
-        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        const float z[4] = {bf16_lo(zb[b][jg][0]), bf16_hi(zb[b][jg][0]),
-                            bf16_lo(zb[b][jg][1]), bf16_hi(zb[b][jg][1])};
-        const float u[4] = {bf16_lo(ub[b][jg][0]), bf16_hi(ub[b][jg][0]),
-                            bf16_lo(ub[b][jg][1]), bf16_hi(ub[b][jg][1])};
-        float d1[4], d3[4];
+    auto get4 = [&](const char* st, int r, int c, float (&v)[4]) {
+      const uint32_t o = (uint32_t)r * RS + ((uint32_t)((c >> 3) ^ (r & 15)) << 4) + ((c >> 2) & 1) * 8;
+      const u32x2 w2 = *reinterpret_cast<const u32x2*>(st + o);
+      v[0] = bf16_lo(w2[0]); v[1] = bf16_hi(w2[0]); v[2] = bf16_lo(w2[1]); v[3] = bf16_hi(w2[1]);
+    };
+    // NR staged rows -> memory; staged row q is tile row rowmap(q).  Each
+    // instruction of the block covers RPI whole rows; wavefront w takes every
+    // fourth one.
+    auto store_rows = [&](const char* st, auto nr_tag, void* C, auto rowmap) {
+      constexpr int NR = decltype(nr_tag)::value;
+      const int c = lane % LPR, col = n0 + 8 * c;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float v = acc[0][i][j][4 * g + t];
-          const float sg = sigmoid_f(z[t]);
-          d1[t] = v * u[t] * sg * (1.0f + z[t] * (1.0f - sg));
-          d3[t] = v * z[t] * sg;
+      for (int it = 0; it < NR / (4 * RPI); ++it) {
+        const int q = (it * 4 + w) * RPI + lane / LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + (uint32_t)q * RS + ((uint32_t)(c ^ (q & 15)) << 4));
+        const int r = rowmap(q);
+        if (r < valid && col < p.N)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + (row0 + r) * p.ldc + col) = v;
+      }
+    };
+    using R128 = std::integral_constant<int, 128>;
+    using R256 = std::integral_constant<int, 256>;
+    using R64 = std::integral_constant<int, 64>;
+
+    if constexpr (EPI == EPI_F32) {
+      // fp32 weight gradient of expert e (K-grouped): rows of BN floats
+      // (RF bytes, 16-byte chunk c of row r at c ^ (r & 15)), non-temporal
+      // whole-row stores.  One output of 256 rows x 128 columns fills both
+      // stages (rows 0-127 and 128-255); a 256-column output goes in two
+      // halves, one per wavefront row.
+      constexpr int RF = BN * 4, LPRF = BN / 4, RPIF = 64 / LPRF;
+      constexpr int kHalfRows = 64 * 1024 / RF;        // staged rows per stage
+      constexpr int kRound = 2 * kHalfRows;            // staged rows per round
+      static_assert(kRound == 128 || kRound == 256, "fp32 staging");
+      float* gbase = reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe;
+      auto put_f4 = [&](int q, int c, const float (&v)[4]) {
+        char* st = q < kHalfRows ? stage0 : stage1;
+        const int ql = q < kHalfRows ? q : q - kHalfRows;
+        const uint32_t o = (uint32_t)ql * RF + ((uint32_t)((c >> 2) ^ (ql & 15)) << 4);
+        *reinterpret_cast<f32x4*>(st + o) = f32x4{v[0], v[1], v[2], v[3]};
+      };
+      auto store_round = [&](float* C, int rbase) __attribute__((always_inline)) {
+        const int c = lane % LPRF, col = n0 + 4 * c;
+#pragma unroll
+        for (int it = 0; it < kRound / (4 * RPIF); ++it) {
+          const int q = (it * 4 + w) * RPIF + lane / LPRF;
+          const char* st = q < kHalfRows ? stage0 : stage1;
+          const int ql = q < kHalfRows ? q : q - kHalfRows;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(st + (uint32_t)ql * RF + ((uint32_t)(c ^ (ql & 15)) << 4));
+          const int r = m0 + rbase + q;
+          if (r < p.M && col < p.N)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (int64_t)r * p.ldc + col));
         }
-        if (row_ok && c < p.N) {
-          store4_bf16(p.C0, ro + c, d1);
-          store4_bf16(p.C1, ro + c, d3);
-        }
+      };
+      if constexpr (kRound == 256) {
+        // dual: each output tile is one round written by all four wavefronts
+        static_assert(DUAL, "256-row rounds hold a 128-column output");
+        StaticFor<0, NB>::run([&](auto b_tag) {
+          constexpr int b = decltype(b_tag)::value;
+          if constexpr (b > 0) __syncthreads();
+          StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+            constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+            const float v[4] = {acc[b][i][j][4 * g], acc[b][i][j][4 * g + 1], acc[b][i][j][4 * g + 2],
+                                acc[b][i][j][4 * g + 3]};
+            put_f4(wm * WM + i * 32 + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+          });
+          __syncthreads();
+          store_round((b ? reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe : gbase), 0);
+        });
+      } else {
+        // one output of 256 columns: wavefront row hh stages its 128 rows
+        static_assert(!DUAL && BM == 256, "128-row rounds hold half a 256-column output");
+        StaticFor<0, 2>::run([&](auto h_tag) {
+          constexpr int hh = decltype(h_tag)::value;
+          if constexpr (hh > 0) __syncthreads();
+          if (wm == hh) {
+            StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+              constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+              const float v[4] = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
+                                  acc[0][i][j][4 * g + 3]};
+              put_f4(i * 32 + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+            });
+          }
+          __syncthreads();
+          store_round(gbase, hh * 128);
+        });
+      }
+    } else if constexpr (EPI == EPI_STORE) {
+      // rows 0-127 in stage 0, 128-255 in stage 1 (the wavefront row wm)
+      static_assert(NB == 1 && BM == 256, "store epilogue tile");
+      char* st = wm ? stage1 : stage0;
+      StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+        constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+        const float v[4] = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
+                            acc[0][i][j][4 * g + 3]};
+        put4(st, i * 32 + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
       });
-    });
-  } else if constexpr (kSwapAB) {
-    StaticFor<0, MI>::run([&](auto i_tag) {
-      constexpr int i = decltype(i_tag)::value;
-      const int r = wm * WM + i * 32 + (lane & 31);
-      const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
-      const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
-      StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
-        constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
-        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        float v0[4], v1[4];
+      __syncthreads();
+      store_rows(stage0, R128{}, p.C0, [](int q) { return q; });
+      store_rows(stage1, R128{}, p.C0, [](int q) { return q + 128; });
+    } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+      // h1 in stage 0 and a = silu(h1) h3 in stage 1 (256 rows x 128 columns
+      // each; a from the fp32 accumulators), then h3 in stage 0
+      static_assert(NB == 2 && BM == 256 && BN == 128, "SwiGLU epilogue tile");
+      StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+        constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+        const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        float v0[4], a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           v0[t] = acc[0][i][j][4 * g + t];
-          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
+          a[t] = silu_f(v0[t]) * acc[1][i][j][4 * g + t];
         }
-        if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
+        put4(stage0, r, c, v0);
+        put4(stage1, r, c, a);
       });
-    });
+      __syncthreads();
+      store_rows(stage0, R256{}, p.C0, [](int q) { return q; });
+      store_rows(stage1, R256{}, p.C2, [](int q) { return q; });
+      __syncthreads();
+      StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+        constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+        const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        const float v1[4] = {acc[1][i][j][4 * g], acc[1][i][j][4 * g + 1], acc[1][i][j][4 * g + 2],
+                             acc[1][i][j][4 * g + 3]};
+        put4(stage0, r, c, v1);
+      });
+      __syncthreads();
+      store_rows(stage0, R256{}, p.C1, [](int q) { return q; });
+    } else {
+      // SwiGLU backward: four phases, one per 32-row group i of both
+      // wavefront rows (64 tile rows).  A phase's h1 and h3 rows (32 KB each)
+      // come into one stage with coalesced loads while the previous phase is
+      // computed from the other; dh1 and dh3 overwrite them in place and
+      // leave as whole rows.
+      static_assert(EPI == EPI_SWIGLU_BWD && NB == 1 && BM == 256 && BN == 256, "dA epilogue tile");
+      constexpr int kHalfB = 64 * RS;                  // one matrix of a phase in a stage
+      constexpr int kLd = 2 * 64 * LPR / kThreads4;    // 16-byte loads per lane per phase
+      const uint16_t* h1 = reinterpret_cast<const uint16_t*>(p.X0);
+      const uint16_t* h3 = reinterpret_cast<const uint16_t*>(p.X1);
+      // staged row q of a phase holds tile row (q / 32) * 128 + 32 i + q % 32
+      auto tile_row = [](int i, int q) { return (q >> 5) * 128 + i * 32 + (q & 31); };
+      u32x4 pre[kLd];
+      auto load_phase = [&](int i) {
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+          const int f = u * kThreads4 + tid;           // 16-byte piece of the phase
+          const int m = f / (64 * LPR), q = (f / LPR) % 64, c = f % LPR;
+          // rows past the tile's valid ones read row 0 (never stored)
+          const int r = tile_row(i, q);
+          const int64_t o = (row0 + (r < valid ? r : 0)) * p.ldc + min(n0 + 8 * c, p.N - 8);
+          pre[u] = *reinterpret_cast<const u32x4*>((m ? h3 : h1) + o);
+        }
+      };
+      auto put_phase = [&](char* st) {
+#pragma unroll
+        for (int u = 0; u < kLd; ++u) {
+          const int f = u * kThreads4 + tid;
+          const int m = f / (64 * LPR), q = (f / LPR) % 64, c = f % LPR;
+          *reinterpret_cast<u32x4*>(st + m * kHalfB + (uint32_t)q * RS + ((uint32_t)(c ^ (q & 15)) << 4)) = pre[u];
+        }
+      };
+      load_phase(0);
+      put_phase(stage0);
+      StaticFor<0, MI>::run([&](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value;
+        char* st = (i & 1) ? stage1 : stage0;
+        if constexpr (i + 1 < MI) load_phase(i + 1);
+        __syncthreads();
+        const int q = wm * 32 + (lane & 31);
+        StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
+          constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
+          const int c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          float z[4], u[4], d1[4], d3[4];
+          get4(st, q, c, z);
+          get4(st + kHalfB, q, c, u);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float v = acc[0][i][j][4 * g + t];
+            const float sg = sigmoid_f(z[t]);
+            const float vs = v * sg;
+            d3[t] = vs * z[t];
+            d1[t] = vs * u[t] * (1.0f + z[t] - z[t] * sg);
+          }
+          put4(st, q, c, d1);
+          put4(st + kHalfB, q, c, d3);
+        });
+        __syncthreads();
+        store_rows(st, R64{}, p.C0, [&](int qq) { return tile_row(i, qq); });
+        store_rows(st + kHalfB, R64{}, p.C1, [&](int qq) { return tile_row(i, qq); });
+        if constexpr (i + 1 < MI) put_phase((i & 1) ? stage0 : stage1);
+      });
+    }
   } else {
     // direct 32x32 result: lane holds column (lane % 32), rows 8 (v/4) + 4 (lane/32) + v%4
     StaticFor<0, MI * NJ>::run([&](auto ij_tag) {
