@@ -81,6 +81,11 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.dwg_items = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * 16);
   L.dwg_estart = off; off = align256(off + (size_t)(E + 1) * 4);
   L.dwg_part = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * H * 4);
+  // the products with a bf16 store epilogue (down, dxd) split the tiles of a
+  // partial last wave along K: at most 256 partial tiles, and at most eight
+  // per tile the problem can have
+  L.tail_items = (int)std::min<int64_t>(256, (int64_t)8 * L.max_tiles * ((H + 255) / 256));
+  L.gemm_part = off; off = align256(off + (size_t)std::max(L.tail_items, 1) * 256 * 256 * 4);
   L.total = off;
   return L;
 }

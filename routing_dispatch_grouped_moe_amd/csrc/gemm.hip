@@ -86,6 +86,9 @@ struct GemmArgs {
   const void* X0;         // h1, h3 for the SwiGLU backward epilogue
   const void* X1;
   int accum;
+  float* part;            // K-split partial tiles of the last wave (store epilogue)
+  int tail_cap;           // capacity of part in tiles
+  int ncu;                // compute units of the device (tiles in flight per wave)
 };
 
 // ------------------------------------------------------------- epilogue --
@@ -167,6 +170,73 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& p, int e, int64_t row,
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   const int x = b & 7, q = nb >> 3, r = nb & 7;
   return x * q + min(x, r) + (b >> 3);
+}
+
+// M-grouped tile t of T = ntiles * ntn: groups of kGroupM M tiles (fewer in
+// the last group) walked with the M tile fastest.
+__device__ __forceinline__ void mtile_of(int t, int ntiles, int ntn, int& mt, int& nt) {
+  const int per_group = kGroupM * ntn, g4 = ntiles / kGroupM * per_group;
+  if (t < g4) {
+    const int g = t / per_group, r = t - g * per_group;
+    mt = g * kGroupM + r % kGroupM;
+    nt = r / kGroupM;
+  } else {
+    const int r = t - g4, gm = ntiles % kGroupM;
+    mt = ntiles / kGroupM * kGroupM + r % gm;
+    nt = r / gm;
+  }
+}
+
+// Last-wave K split.  With T tiles on ncu compute units, a last wave of
+// rem = T mod ncu tiles (at most half a wave) leaves most units idle for a
+// whole tile time; those tiles are split along K into s parts (s rem blocks
+// after the T - rem whole tiles), each part writes an fp32 partial tile and
+// a second kernel sums the parts in order.  Both kernels derive the plan
+// from the same inputs.
+struct SplitPlan {
+  int full;  // whole tiles (block ids 0 .. full-1)
+  int rem;   // tiles of the last wave that are split
+  int s;     // parts per split tile (1: no split)
+};
+constexpr int kMaxSplit = 8, kMinSplitSteps = 16;
+__device__ __forceinline__ SplitPlan split_plan(const GemmArgs& p, int nk2) {
+  const int T = *p.ntiles * p.ntn;
+  SplitPlan sp{T, 0, 1};
+  const int rem = p.ncu > 0 ? T % p.ncu : 0;
+  if (rem > 0 && 2 * rem <= p.ncu) {
+    const int s = min(min(p.ncu / rem, kMaxSplit), min(p.tail_cap / rem, nk2 / kMinSplitSteps));
+    if (s >= 2) sp = SplitPlan{T - rem, rem, s};
+  }
+  return sp;
+}
+
+// Tile of block bid of an M-grouped launch that may split its last wave;
+// part = -1 for a whole tile, else the K part (item = its partial tile).
+template <int BM, int BN, bool SPLIT>
+__device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2, int& e,
+                                            int64_t& row0, int& valid, int& n0, int& part,
+                                            int& item, int& nparts) {
+  SplitPlan sp{*p.ntiles * p.ntn, 0, 1};
+  if constexpr (SPLIT) sp = split_plan(p, nk2);
+  part = -1; item = 0; nparts = sp.s;
+  int t;
+  if (bid < sp.full) {
+    t = xcd_remap(bid, sp.full);
+  } else {
+    const int j = bid - sp.full;
+    if (j >= sp.rem * sp.s) return false;
+    t = sp.full + j / sp.s;
+    part = j % sp.s;
+    item = j;
+  }
+  int mt, nt;
+  mtile_of(t, *p.ntiles, p.ntn, mt, nt);
+  n0 = nt * BN;
+  const int2 tt = p.tiles[mt];
+  e = tt.x;
+  row0 = (int64_t)p.cu[e] + tt.y;
+  valid = min(BM, p.cu[e + 1] - (int)row0);
+  return true;
 }
 
 template <bool KGROUP, int BM, int BN>
@@ -618,9 +688,19 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char stage0[kStage];
   __shared__ __attribute__((aligned(1024))) char stage1[kStage];
 
-  int e, valid, m0, n0;
+  // products with a plain store epilogue split the tiles of a partial last
+  // wave along K (fp32 partial tiles, summed by tail_reduce_kernel)
+  constexpr bool kSplit = !KGROUP && EPI == EPI_STORE;
+  int e, valid, m0 = 0, n0, part = -1, item = 0, nparts = 1;
   int64_t row0;
-  if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  if constexpr (KGROUP) {
+    if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  } else {
+    const int nks = p.K / kBK, nkt = TWOSEG ? 2 * nks : nks;
+    if (!mtile_split<BM, BN, kSplit>(p, blockIdx.x, (nkt + 1) & ~1, e, row0, valid, n0, part, item,
+                                     nparts))
+      return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
@@ -777,20 +857,30 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     slice(af1, bf1, nxt, 0, af0, bf0, ra2, rb2, cur, 0, T{});
   };
 
+  // K steps [k_lo, k_end) of this block: all of them, or one part of a split
+  // tile (even boundaries, so the two-stage unroll holds)
+  const int nk2 = (nk + 1) & ~1;
+  int k_lo = 0, k_end = nk2;
+  if constexpr (kSplit) {
+    if (part >= 0) {
+      const int pairs = nk2 >> 1;
+      k_lo = 2 * (part * pairs / nparts);
+      k_end = 2 * ((part + 1) * pairs / nparts);
+    }
+  }
   {
     u32x4 ra[1], rb[NB];
-    step_rsrc(0, ra, rb);
+    step_rsrc(k_lo, ra, rb);
 #pragma unroll
     for (int t = 0; t < kDma; ++t) issue_one(t, ra, rb, stage0);
-    step_rsrc(1, ra, rb);
+    step_rsrc(k_lo + 1, ra, rb);
 #pragma unroll
     for (int t = 0; t < kHalf; ++t) issue_one(t, ra, rb, stage1);
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kHalf) : "memory");
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) read_frag(stage0, 0, f, af0, bf0);
-  const int nk2 = (nk + 1) & ~1;
-  for (int kt = 0; kt < nk2; kt += 2) {
+  for (int kt = k_lo; kt < k_end; kt += 2) {
     step(kt, I0{});
     step(kt + 1, I1{});
   }
@@ -803,6 +893,20 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // Written straight to memory, one such store instruction touches 32 rows
   // with 16 bytes each; the bf16 outputs are instead staged through the two
   // (now free) 64-KB LDS stages and leave as whole rows, 16 bytes a lane.
+  if constexpr (kSplit) {
+    if (part >= 0) {
+      // one K part of a split tile: the fp32 accumulators in fragment order
+      // (each store instruction writes 1 KB contiguous)
+      f32x4* dst = reinterpret_cast<f32x4*>(p.part) + (size_t)item * (BM * BN / 4);
+      StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+        constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+        dst[(((w * MI + i) * NJ + j) * 4 + g) * 64 + lane] =
+            f32x4{acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
+                  acc[0][i][j][4 * g + 3]};
+      });
+      return;
+    }
+  }
   if constexpr (kSwapAB) {
     static_assert(!KGROUP || EPI == EPI_F32, "staged epilogue kinds");
     // every direct load has landed and every wavefront is done with the stages
@@ -1033,6 +1137,45 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
 #endif
 }
 
+// Sums the K parts of each split tile (in part order) and stores the bf16
+// result.  Block (tile tt, 32-row group i); thread (w, lane) takes the
+// accumulators that wavefront w, lane held in the GEMM: row
+// (w / 2) * WM + 32 i + lane % 32, columns (w % 2) * WN + 32 j + 8 g + 4 (lane / 32) + t.
+template <int BM, int BN, bool TWOSEG>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
+  constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NJ = WN / 32;
+  const int nks = p.K / kBK, nkt = TWOSEG ? 2 * nks : nks;
+  const SplitPlan sp = split_plan(p, (nkt + 1) & ~1);
+  const int tt = blockIdx.x / MI, i = blockIdx.x % MI;
+  if (sp.s < 2 || tt >= sp.rem) return;
+  int mt, nt;
+  mtile_of(sp.full + tt, *p.ntiles, p.ntn, mt, nt);
+  const int2 tl = p.tiles[mt];
+  const int64_t row0 = (int64_t)p.cu[tl.x] + tl.y;
+  const int valid = min(BM, p.cu[tl.x + 1] - (int)row0);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int r = (w >> 1) * WM + i * 32 + (lane & 31);
+  if (r >= valid) return;
+  constexpr size_t kTile = BM * BN / 4;
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.part) + (size_t)tt * sp.s * kTile +
+                     (size_t)((w * MI + i) * NJ * 4) * 64 + lane;
+  // part by part, all NJ * 4 pieces of a part in flight together
+  f32x4 a[NJ * 4];
+#pragma unroll
+  for (int x = 0; x < NJ * 4; ++x) a[x] = src[x * 64];
+  for (int k = 1; k < sp.s; ++k) {
+#pragma unroll
+    for (int x = 0; x < NJ * 4; ++x) a[x] += src[k * kTile + x * 64];
+  }
+#pragma unroll
+  for (int x = 0; x < NJ * 4; ++x) {
+    const int j = x / 4, g = x % 4;
+    const int col = nt * BN + (w & 1) * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+    const float v[4] = {a[x][0], a[x][1], a[x][2], a[x][3]};
+    if (col < p.N) store4_bf16(p.C0, (row0 + r) * p.ldc + col, v);
+  }
+}
+
 // ---------------------------------------------------------- fp32 kernel --
 // M tile of kGemmBM rows x 32 columns; thread (tid % 32) owns a column,
 // rows tid/32 + 8 i.
@@ -1135,6 +1278,12 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
     const int groups = (max_mtiles + kGroupM - 1) / kGroupM;
     blocks = groups * kGroupM * p.ntn;
   }
+  // a split last wave adds at most tail_cap blocks (its rem tiles become
+  // s * rem parts, s * rem <= tail_cap)
+  constexpr bool kSplit = !KGROUP && EPI == EPI_STORE;
+  const bool split = kSplit && bf16 && W4 && p.part != nullptr && p.tail_cap > 0 && p.ncu > 0;
+  if (kSplit && !split) p.ncu = 0;
+  if (split) blocks += p.tail_cap;
   if (blocks <= 0) return;
   TimedLaunch tl(name, s);
   if (bf16) {
@@ -1146,6 +1295,12 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
       // SIMD's register file next to 256 accumulators)
       auto kern = gemm_bf16_w4_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads4), 0, s, p);
+      if constexpr (kSplit) {
+        // at most tail_cap / 2 split tiles (each has at least two parts)
+        if (split)
+          hipLaunchKernelGGL((tail_reduce_kernel<BM, BN, TWOSEG>), dim3(p.tail_cap / 2 * (BM / 64)),
+                             dim3(256), 0, s, p);
+      }
     } else {
       auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
       // a failure stays the thread's last HIP error (so the entry point
@@ -1167,6 +1322,26 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
 // and the eight-wavefront form (no even-step rounding, shorter per-tile
 // set-up) is faster.  The host knows the mean without reading the counts.
 static bool many_rows(int64_t R, int E) { return R >= (int64_t)1024 * E; }
+
+// Compute units of the current device (cached per device; 0 if unknown,
+// which turns the last-wave split off).
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+static void split_args(GemmArgs& p, const WsLayout& L, char* ws) {
+  p.part = reinterpret_cast<float*>(ws + L.gemm_part);
+  p.tail_cap = L.tail_items;
+  p.ncu = device_cus();
+}
 
 static GemmArgs base_args(const int32_t* cu, const WsLayout& L, char* ws, int E) {
   GemmArgs p{};
@@ -1200,6 +1375,7 @@ void launch_ffn_down(const void* a, const int32_t* cu, const void* W2, void* y, 
   p.A0 = a; p.lda = Hf;
   p.B0 = W2; p.ldb = H; p.sBe = (int64_t)Hf * H;
   p.C0 = y; p.ldc = H;
+  split_args(p, L, ws);
   gemm_launch<256, 256, true, false, false, false, false, EPI_STORE>("ffn_down", p, L.max_tiles,
                                                                      bf16, s);
 }
@@ -1229,6 +1405,7 @@ void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const v
   p.A0 = dh1; p.A1 = dh3; p.lda = Hf;
   p.B0 = W1; p.B1 = W3; p.ldb = Hf; p.sBe = (int64_t)H * Hf;
   p.C0 = dxd; p.ldc = H;
+  split_args(p, L, ws);
   gemm_launch<256, 256, true, true, false, true, false, EPI_STORE>("bwd_dxd", p, L.max_tiles, bf16,
                                                                    s);
 }

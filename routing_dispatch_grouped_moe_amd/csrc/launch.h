@@ -31,12 +31,14 @@ struct WsLayout {
   size_t dwg_items;   // [dwg_max_items] int4 (expert, first row, rows, 0) row items of dWg
   size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
   size_t dwg_part;    // [dwg_max_items, H] fp32 partial router-weight gradient per item
+  size_t gemm_part;   // [tail_items, 256 * 256] fp32 K-split partial tiles of the last GEMM wave
   size_t total;
   int nb;             // dispatch blocks of 256 tokens
   int epad;           // E rounded up to 16
   int max_tiles;      // upper bound on M tiles over all experts
   int dwg_rb;         // rows per dWg item (a power of two, 16..256)
   int dwg_max_items;  // upper bound on dWg items over all experts
+  int tail_items;     // capacity of gemm_part in partial tiles
 };
 WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
 

@@ -93,6 +93,10 @@ CASES = [
     # few-rows bound of the weight-gradient products (smaller shares use the
     # small-tile form)
     ("c2_mixtral_shape_multi_tile", "c2", dict(S=2100, H=256, Hf=384)),
+    # about 24 tiles, under half a wave of 256 compute units: the down and dxd
+    # products split every tile along K (2 and 4 parts; H' = 2048 gives 32
+    # and 64 K steps) and sum fp32 partial tiles in a second kernel
+    ("c2_k_split_last_wave", "c2", dict(S=2100, H=256, Hf=2048, E=12)),
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
@@ -112,8 +116,11 @@ def test_layer_parity(cid, cfg, ov):
         assert flips == 0
 
 
-def test_determinism_bitwise():
-    wl = make_workload("c3", S=257, H=256, Hf=256, host_weights=True)
+@pytest.mark.parametrize("cfg,ov", [("c3", dict(S=257, H=256, Hf=256)),
+                                    ("c2", dict(S=2100, H=256, Hf=2048, E=12))],
+                         ids=["c3_small", "c2_k_split"])
+def test_determinism_bitwise(cfg, ov):
+    wl = make_workload(cfg, **ov, host_weights=True)
     a = run_layer(wl)
     b = run_layer(wl)
     for k in a:
