@@ -88,6 +88,35 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Descriptor words (uniform, for an "s" operand of inline assembly) of the
+// byte range [base, base + bytes): reads past it return zero.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+// Direct global -> LDS loads: lane l reads 4 (dma4) or 16 (dma16) bytes at
+// byte offset voff of the descriptor's range and writes them to LDS at
+// dst + 4 l (16 l).  Issued from inline assembly: the compiler neither
+// treats them as LDS stores nor makes LDS reads wait on them, so the caller
+// waits for them (vmcnt) before the barrier that publishes the data, and
+// only ever targets LDS that no wavefront is reading.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, const void* dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_addr(dst)) : "m0");
+}
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, const void* dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_addr(dst)) : "m0");
+}
+
 // ------------------------------------------------------- wave reductions --
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

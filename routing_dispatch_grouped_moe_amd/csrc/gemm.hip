@@ -404,12 +404,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
-  // bf16 outputs take the transposed MFMA result (four consecutive columns
-  // per lane, 8-byte pieces); the fp32 weight gradients keep the direct one,
-  // where each 4-byte store instruction writes two whole 128-byte rows,
-  // which suits these write-bound products better than 16-byte pieces
-  // scattered over 32 rows
-  constexpr bool kSwapAB = !epi_f32(EPI);
+  // The transposed MFMA result (four consecutive columns per lane) for every
+  // kind but the accumulating weight gradient, which keeps the direct one
+  // (each 4-byte store instruction covers two whole 128-byte rows).  The
+  // overwriting weight gradient is staged through LDS and leaves as whole
+  // rows.
+  constexpr bool kSwapAB = EPI != EPI_F32_ACC;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
@@ -544,7 +544,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     lds_barrier();
   }
 
-  if constexpr (kSwapAB) {
+  if constexpr (EPI == EPI_F32) {
+    // fp32 weight gradient of expert e: the 2 x kStage bytes of LDS (free
+    // after the loop's last barrier) hold kRound rows of BN floats (RF
+    // bytes, 16-byte chunk c of row q at c ^ (q & 15)); non-temporal
+    // whole-row stores.  A 128-column output (dual) is one round per operand
+    // written by all wavefronts, a 256-column output two rounds of 128 rows
+    // (wavefront row wm stages round wm).
+    constexpr int RF = BN * 4, LPRF = BN / 4, RPIF = 64 / LPRF;
+    constexpr int kRound = 2 * kStage / RF;
+    static_assert(kRound == 256 || (kRound == 128 && !DUAL && BM == 256), "fp32 staging rounds");
+    auto put_f4 = [&](int q, int c, const float (&v)[4]) {
+      *reinterpret_cast<f32x4*>(smem + (uint32_t)q * RF + ((uint32_t)((c >> 2) ^ (q & 15)) << 4)) =
+          f32x4{v[0], v[1], v[2], v[3]};
+    };
+    auto store_round = [&](float* C, int rbase) __attribute__((always_inline)) {
+      const int c = lane % LPRF, col = n0 + 4 * c;
+#pragma unroll
+      for (int it = 0; it < kRound / (8 * RPIF); ++it) {
+        const int q = (it * 8 + w) * RPIF + lane / LPRF;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + (uint32_t)q * RF + ((uint32_t)(c ^ (q & 15)) << 4));
+        const int r = m0 + rbase + q;
+        if (r < p.M && col < p.N)
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (int64_t)r * p.ldc + col));
+      }
+    };
+    constexpr int kRounds = kRound == 256 ? NB : 2;
+    StaticFor<0, kRounds>::run([&](auto r_tag) {
+      constexpr int rd = decltype(r_tag)::value;
+      constexpr int b = kRound == 256 ? rd : 0;
+      if constexpr (rd > 0) lds_barrier();
+      if (kRound == 256 || wm == rd) {
+        StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+          constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+          const float v[4] = {acc[b][i][j][4 * g], acc[b][i][j][4 * g + 1], acc[b][i][j][4 * g + 2],
+                              acc[b][i][j][4 * g + 3]};
+          put_f4((kRound == 256 ? wm * WM : 0) + i * 32 + (lane & 31),
+                 wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+        });
+      }
+      lds_barrier();
+      float* C = reinterpret_cast<float*>(b ? p.C1 : p.C0) + (int64_t)e * p.sCe;
+      store_round(C, kRound == 256 ? 0 : rd * 128);
+    });
+  } else if constexpr (kSwapAB) {
     // transposed 32x32 result: lane l holds row (l % 32) and, for v = 4g + t,
     // column 8 g + 4 (l / 32) + t
 StaticFor<0, MI>::run([&](auto i_tag) {

@@ -14,6 +14,8 @@
 // keys (ordered logit bits : ~expert), and K rounds of a butterfly max pick
 // the winners.  Counts come from an LDS histogram flushed with one atomic
 // per (block, expert).
+#include <algorithm>
+
 #include "dev_common.h"
 #include "launch.h"
 #include "moe.h"
@@ -74,105 +76,64 @@ void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool
     hipLaunchKernelGGL(transpose_wg_kernel<false>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad);
 }
 
-// Column blocks of 16 experts per wave and H slices per wave for a given Epad.
+// ------------------------------------------------------------ router GEMM --
+// Waves split the 16-expert column blocks (nwn of them side by side, NCB
+// blocks each) and, when there are fewer than four column blocks, the K
+// range (KS waves along K); U K32 sub-slices per wave per stage keep the
+// stages of small routers from being tiny.
 struct RouteSplit {
-  int nwn, ks, ncb;
+  int nwn, ks, ncb, u;
 };
-__host__ __device__ inline RouteSplit route_split(int epad, bool bf16) {
-  RouteSplit r;
+inline RouteSplit route_split(int epad) {
   const int nb = epad / 16;
-  if (!bf16) { r.nwn = 4; r.ks = 1; r.ncb = 0; return r; }
-  r.nwn = nb < 4 ? nb : 4;
+  RouteSplit r;
+  r.nwn = nb >= 4 ? 4 : (nb >= 2 ? 2 : 1);
   r.ks = 4 / r.nwn;
   r.ncb = (nb + r.nwn - 1) / r.nwn;
+  r.u = (r.ks == 1 && r.ncb <= 2) ? 2 : 1;
   return r;
 }
 
-template <bool BF16, int NCB>
-__global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ x,
-                                                    const void* __restrict__ wgT,
-                                                    const float* __restrict__ bias,
-                                                    float* __restrict__ logits,
-                                                    int32_t* __restrict__ idx,
-                                                    float* __restrict__ gates,
-                                                    int32_t* __restrict__ counts,
-                                                    uint32_t* __restrict__ status, int S, int H,
-                                                    int E, int epad, int K, int renorm) {
-  extern __shared__ float part[];  // [ks][BT][epad] partial logits; slice 0 ends up holding logits
-  __shared__ int hist[1024];
+// LDS pipeline of the bf16 router GEMM.  A stage holds one K slice of BK
+// elements: the x tile [32 tokens][BK] (shared by all wavefronts) and, per
+// wavefront, its NCB column blocks x U sub-slices of router-weight rows
+// ([16][32] each, 1 KB).  Every wavefront issues the same kNI direct loads per
+// stage (kXI 256-byte loads of x, NCB U 1-KB loads of its own weight rows),
+// so each one can wait for its own loads of a stage with one vmcnt.
+template <int NCB, int KS, int U>
+struct RouteTile {
+  static constexpr int BK = 32 * KS * U;
+  static constexpr int kXB = kRouteBT * BK * 2;
+  static constexpr int kWB = NCB * U * 1024;
+  static constexpr int kStage = kXB + 4 * kWB;
+  static constexpr int kXI = kXB / 1024;
+  static constexpr int kNI = kXI + NCB * U;
+  static constexpr int NS0 = (104 * 1024) / kStage;
+  static constexpr int NS1 = NS0 < 2 ? 2 : (NS0 > 8 ? 8 : NS0);
+  // a wavefront waits with vmcnt((NS - 2) kNI), and vmcnt counts to 63
+  static constexpr int NS = (NS1 - 2) * kNI <= 63 ? NS1 : 2 + 63 / kNI;
+  static constexpr int CPR = BK / 8;  // 16-byte chunks per x row
+};
+// x rows: 16-byte chunk c of row r stored at c ^ xswz(r), which keeps a
+// 16x16x32 fragment read (16 rows x 4 chunks) on all 16 bank groups per
+// 16 lanes.  Weight rows are 64 bytes (four chunks): c ^ ((r >> 2) & 3).
+template <int CPR>
+__device__ __forceinline__ int xswz(int r) {
+  return CPR == 4 ? (r >> 2) & 3 : CPR == 8 ? (r >> 1) & 7 : r & 15;
+}
+
+// Bias, logits, softmax, top-K and counts of the block's tokens from the
+// partial logits part[ks][32][epad] (summed in slice order).
+__device__ __forceinline__ void route_tail(float* part, int* hist, int ks, const float* bias,
+                                           float* logits, int32_t* idx, float* gates,
+                                           int32_t* counts, uint32_t* status, int t0, int nt,
+                                           int E, int epad, int K, int renorm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t0 = blockIdx.x * kRouteBT;
-  const int nt = min(kRouteBT, S - t0);
-  const RouteSplit sp = route_split(epad, BF16);
-
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
-
-  if constexpr (BF16) {
-    const int wn = w % sp.nwn, ks = w / sp.nwn;
-    if (ks < sp.ks) {
-      const int kslice = H / sp.ks, kbeg = ks * kslice;
-      const uint16_t* xb = reinterpret_cast<const uint16_t*>(x) + (int64_t)t0 * H;
-      const __amdgpu_buffer_rsrc_t rx = make_rsrc(xb, (uint32_t)nt * (uint32_t)H * 2u);
-      const uint16_t* wb = reinterpret_cast<const uint16_t*>(wgT);
-      f32x4 acc[2][NCB];
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) acc[0][c] = acc[1][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r16 = lane & 15, kq = (lane >> 4) * 8;
-      const uint32_t aoff0 = ((uint32_t)r16 * H + kq) * 2u;
-      const uint32_t aoff1 = ((uint32_t)(r16 + 16) * H + kq) * 2u;
-      for (int k = kbeg; k < kbeg + kslice; k += 32) {
-        const u32x4 a0 = buf_load16(rx, aoff0 + k * 2u);
-        const u32x4 a1 = buf_load16(rx, aoff1 + k * 2u);
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-          const int nbk = wn + c * sp.nwn;
-          if (nbk * 16 < epad) {
-            const int n = nbk * 16 + r16;
-            const u32x4 b = *reinterpret_cast<const u32x4*>(wb + (int64_t)n * H + k + kq);
-            acc[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b), acc[0][c], 0, 0, 0);
-            acc[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b), acc[1][c], 0, 0, 0);
-          }
-        }
-      }
-      // 16x16 MFMA result: lane holds column (lane % 16), rows 4*(lane/16) + i.
-      float* pk = part + (size_t)ks * kRouteBT * epad;
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const int nbk = wn + c * sp.nwn;
-        if (nbk * 16 < epad) {
-          const int col = nbk * 16 + r16;
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[(rb * 16 + (lane >> 4) * 4 + i) * epad + col] = acc[rb][c][i];
-        }
-      }
-    }
-  } else {
-    // fp32 storage: plain dot products, one (token, expert) pair per thread.
-    const float* xf = reinterpret_cast<const float*>(x);
-    const float* wf = reinterpret_cast<const float*>(wgT);
-    for (int i = tid; i < kRouteBT * E; i += 256) {
-      const int t = i / E, e = i % E;
-      float acc = 0.f;
-      if (t < nt) {
-        const float* xr = xf + (int64_t)(t0 + t) * H;
-        const float* wr = wf + (int64_t)e * H;
-        for (int h = 0; h < H; ++h) acc = fmaf(xr[h], wr[h], acc);
-      }
-      part[t * epad + e] = acc;
-    }
-  }
-  __syncthreads();
-
-  // Sum the H slices in slice order, add the bias, store the logits.
   uint32_t bad = 0;
   for (int i = tid; i < nt * E; i += 256) {
     const int t = i / E, e = i % E;
     float v = part[t * epad + e];
-    for (int k2 = 1; k2 < sp.ks; ++k2) v += part[((size_t)k2 * kRouteBT + t) * epad + e];
+    for (int k2 = 1; k2 < ks; ++k2) v += part[((size_t)k2 * kRouteBT + t) * epad + e];
     if (bias) v += bias[e];
     part[t * epad + e] = v;
     if (!isfinite(v)) bad = 1;
@@ -230,19 +191,165 @@ __global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ x,
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
-template <bool BF16, int NCB>
+// bf16 router: x [S, H] times the transposed weight WgT [epad, H] on
+// v_mfma_f32_16x16x32_bf16, both operands streamed through an NS-stage LDS
+// ring by direct loads; NS - 1 stages are in flight while one is computed.
+template <int NCB, int KS, int U>
+__global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict__ x,
+                                                         const void* __restrict__ wgT,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ gates,
+                                                         int32_t* __restrict__ counts,
+                                                         uint32_t* __restrict__ status, int S,
+                                                         int H, int E, int epad, int K,
+                                                         int renorm) {
+  using T = RouteTile<NCB, KS, U>;
+  constexpr int NWN = 4 / KS;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];  // stages, then partial logits
+  __shared__ int hist[1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = w % NWN, ksi = w / NWN;
+  const int t0 = blockIdx.x * kRouteBT;
+  const int nt = min(kRouteBT, S - t0);
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+
+  // per-lane byte offsets of this wavefront's direct loads (relative to the
+  // stage's K origin)
+  uint32_t vx[T::kXI], vw[NCB * U];
+#pragma unroll
+  for (int i = 0; i < T::kXI; ++i) {
+    const int P = (w * T::kXI + i) * 64 + lane;  // physical dword of the x tile
+    const int row = P / (T::BK / 2), pdw = P % (T::BK / 2);
+    const int c = (pdw >> 2) ^ xswz<T::CPR>(row);
+    vx[i] = ((uint32_t)row * H + c * 8 + (pdw & 3) * 2) * 2u;
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = lane >> 2, c = (lane & 3) ^ ((row >> 2) & 3);
+      const int n = (wn + cb * NWN) * 16 + row;
+      vw[cb * U + u] = ((uint32_t)n * H + ksi * 32 * U + u * 32 + c * 8) * 2u;
+    }
+  const char* xb = reinterpret_cast<const char*>(x) + (int64_t)t0 * H * 2;
+  const char* wb = reinterpret_cast<const char*>(wgT);
+  const uint32_t xbytes = (uint32_t)nt * H * 2u, wbytes = (uint32_t)epad * H * 2u;
+  // loads of K slice kt into stage st (past the end of K they read zeros or
+  // rows of this block's own range, into a stage that is not read again)
+  auto issue = [&](int kt, int st) {
+    const uint32_t k2 = (uint32_t)kt * T::BK * 2u;
+    const u32x4 rx = rsrc_words(xb + k2, xbytes - min(k2, xbytes));
+    const u32x4 rw = rsrc_words(wb + k2, wbytes - min(k2, wbytes));
+    char* sb = smem + st * T::kStage;
+#pragma unroll
+    for (int i = 0; i < T::kXI; ++i) dma4(rx, vx[i], sb + (w * T::kXI + i) * 256);
+#pragma unroll
+    for (int j = 0; j < NCB * U; ++j) dma16(rw, vw[j], sb + T::kXB + w * T::kWB + j * 1024);
+  };
+
+  f32x4 acc[2][NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[0][cb] = acc[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsteps = H / T::BK;
+#pragma unroll
+  for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
+  const int r16 = lane & 15, q = lane >> 4;
+  for (int kt = 0; kt < nsteps; ++kt) {
+    // this wavefront's loads of slice kt landed; after the barrier so have
+    // everyone's, and every wavefront is done with slice kt - 1's stage
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((T::NS - 2) * T::kNI) : "memory");
+    issue(kt + T::NS - 1, (kt + T::NS - 1) % T::NS);
+    const char* sb = smem + (kt % T::NS) * T::kStage;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = ksi * U + u;  // K32 sub-slice of the stage
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(
+          sb + r16 * (T::BK * 2) + (((kk * 4 + q) ^ xswz<T::CPR>(r16)) << 4));
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(
+          sb + (r16 + 16) * (T::BK * 2) + (((kk * 4 + q) ^ xswz<T::CPR>(r16 + 16)) << 4));
+      // column blocks past epad hold zeros (their weight rows lie outside
+      // the descriptor's range): no branch, so all fragment reads go out
+      // before the MFMAs
+      u32x4 b[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        b[cb] = *reinterpret_cast<const u32x4*>(sb + T::kXB + w * T::kWB + (cb * U + u) * 1024 +
+                                                r16 * 64 + ((q ^ ((r16 >> 2) & 3)) << 4));
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b[cb]), acc[0][cb], 0, 0, 0);
+        acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[cb]), acc[1][cb], 0, 0, 0);
+      }
+    }
+  }
+  // every direct load has landed and every wavefront is done with the stages
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // 16x16 MFMA result: lane holds column (lane % 16), rows 4 (lane / 16) + i
+  float* part = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int nbk = wn + cb * NWN;
+    if (nbk * 16 < epad) {
+      const int col = nbk * 16 + r16;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          part[((size_t)ksi * kRouteBT + rb * 16 + q * 4 + i) * epad + col] = acc[rb][cb][i];
+    }
+  }
+  __syncthreads();
+  route_tail(part, hist, KS, bias, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
+}
+
+// fp32 router: plain dot products, one (token, expert) pair per thread.
+__global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
+                                                        const float* __restrict__ wgT,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits,
+                                                        int32_t* __restrict__ idx,
+                                                        float* __restrict__ gates,
+                                                        int32_t* __restrict__ counts,
+                                                        uint32_t* __restrict__ status, int S,
+                                                        int H, int E, int epad, int K, int renorm) {
+  extern __shared__ float fpart[];  // [32][epad]
+  __shared__ int hist[1024];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouteBT;
+  const int nt = min(kRouteBT, S - t0);
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  for (int i = tid; i < kRouteBT * E; i += 256) {
+    const int t = i / E, e = i % E;
+    float acc = 0.f;
+    if (t < nt) {
+      const float* xr = x + (int64_t)(t0 + t) * H;
+      const float* wr = wgT + (int64_t)e * H;
+      for (int h = 0; h < H; ++h) acc = fmaf(xr[h], wr[h], acc);
+    }
+    fpart[t * epad + e] = acc;
+  }
+  __syncthreads();
+  route_tail(fpart, hist, 1, bias, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
+}
+
+template <int NCB, int KS, int U>
 static void route_launch_t(const void* x, const void* wgT, const float* bias, float* logits,
                            int32_t* idx, float* gates, int32_t* counts, uint32_t* status, int64_t S,
                            int H, int E, int epad, int K, bool renorm, hipStream_t s) {
-  const RouteSplit sp = route_split(epad, BF16);
-  const size_t lds = (size_t)sp.ks * kRouteBT * epad * sizeof(float);
-  auto kern = route_kernel<BF16, NCB>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    attr_set = true;
-  }
+  using T = RouteTile<NCB, KS, U>;
+  const size_t lds = std::max((size_t)T::NS * T::kStage, (size_t)KS * kRouteBT * epad * sizeof(float));
+  auto kern = route_mfma_kernel<NCB, KS, U>;
+  // a failure stays the thread's last HIP error (the entry point reports it)
+  static bool attr = false;
+  if (!attr)
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
   const int blocks = (int)((S + kRouteBT - 1) / kRouteBT);
   TimedLaunch tl("route", s);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, s, x, wgT, bias, logits, idx, gates,
@@ -254,18 +361,28 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
                   int epad, int K, bool renorm, bool bf16, hipStream_t s) {
   if (S <= 0) return;
   if (!bf16) {
-    route_launch_t<false, 1>(x, wgT, bias, logits, idx, gates, counts, status, S, H, E, epad, K,
-                             renorm, s);
+    const size_t lds = (size_t)kRouteBT * epad * sizeof(float);
+    static bool attr = false;
+    if (!attr)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_f32_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
+    const int blocks = (int)((S + kRouteBT - 1) / kRouteBT);
+    TimedLaunch tl("route", s);
+    hipLaunchKernelGGL(route_f32_kernel, dim3(blocks), dim3(256), lds, s,
+                       reinterpret_cast<const float*>(x), reinterpret_cast<const float*>(wgT), bias,
+                       logits, idx, gates, counts, status, (int)S, H, E, epad, K, renorm ? 1 : 0);
     return;
   }
-  const int ncb = route_split(epad, true).ncb;
-#define ROUTE_CASE(N)                                                                          \
-  if (ncb <= N) {                                                                              \
-    route_launch_t<true, N>(x, wgT, bias, logits, idx, gates, counts, status, S, H, E, epad, K, \
-                            renorm, s);                                                        \
+  const RouteSplit sp = route_split(epad);
+#define ROUTE_CASE(N, KS_, U_)                                                                  \
+  if (sp.ks == KS_ && sp.u == U_ && sp.ncb <= N) {                                             \
+    route_launch_t<N, KS_, U_>(x, wgT, bias, logits, idx, gates, counts, status, S, H, E, epad, \
+                               K, renorm, s);                                                  \
     return;                                                                                    \
   }
-  ROUTE_CASE(1) ROUTE_CASE(2) ROUTE_CASE(4) ROUTE_CASE(8) ROUTE_CASE(16)
+  ROUTE_CASE(1, 4, 1) ROUTE_CASE(1, 2, 1) ROUTE_CASE(2, 2, 1) ROUTE_CASE(1, 1, 2)
+  ROUTE_CASE(2, 1, 2) ROUTE_CASE(3, 1, 1) ROUTE_CASE(4, 1, 1) ROUTE_CASE(6, 1, 1)
+  ROUTE_CASE(8, 1, 1) ROUTE_CASE(12, 1, 1) ROUTE_CASE(16, 1, 1)
 #undef ROUTE_CASE
 }
 
