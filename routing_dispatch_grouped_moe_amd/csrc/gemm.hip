@@ -400,6 +400,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NB = DUAL ? 2 : 1;
+  constexpr int kWaves = kThreads / 64;
   constexpr int WM = BM / 2, WN = BN / 4;      // wavefront tile (per B operand)
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
@@ -546,14 +547,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 
   if constexpr (EPI == EPI_F32) {
     // fp32 weight gradient of expert e: the 2 x kStage bytes of LDS (free
-    // after the loop's last barrier) hold kRound rows of BN floats (RF
-    // bytes, 16-byte chunk c of row q at c ^ (q & 15)); non-temporal
-    // whole-row stores.  A 128-column output (dual) is one round per operand
-    // written by all wavefronts, a 256-column output two rounds of 128 rows
-    // (wavefront row wm stages round wm).
+    // after the loop's last barrier) hold kRows rows of BN floats (RF bytes,
+    // 16-byte chunk c of row q at c ^ (q & 15)); non-temporal whole-row
+    // stores.  Each operand's BM rows go in BM / kRows rounds; a wavefront
+    // stages the 32-row blocks of its rows that fall in the round.
     constexpr int RF = BN * 4, LPRF = BN / 4, RPIF = 64 / LPRF;
-    constexpr int kRound = 2 * kStage / RF;
-    static_assert(kRound == 256 || (kRound == 128 && !DUAL && BM == 256), "fp32 staging rounds");
+    constexpr int kRows = (2 * kStage / RF) < BM ? (2 * kStage / RF) : BM;
+    constexpr int kRoundsPerOp = BM / kRows;
+    static_assert(kRows % 32 == 0 && BM % kRows == 0 && kRows % (kWaves * RPIF) == 0,
+                  "fp32 staging rounds");
     auto put_f4 = [&](int q, int c, const float (&v)[4]) {
       *reinterpret_cast<f32x4*>(smem + (uint32_t)q * RF + ((uint32_t)((c >> 2) ^ (q & 15)) << 4)) =
           f32x4{v[0], v[1], v[2], v[3]};
@@ -561,31 +563,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     auto store_round = [&](float* C, int rbase) __attribute__((always_inline)) {
       const int c = lane % LPRF, col = n0 + 4 * c;
 #pragma unroll
-      for (int it = 0; it < kRound / (8 * RPIF); ++it) {
-        const int q = (it * 8 + w) * RPIF + lane / LPRF;
+      for (int it = 0; it < kRows / (kWaves * RPIF); ++it) {
+        const int q = (it * kWaves + w) * RPIF + lane / LPRF;
         const f32x4 v = *reinterpret_cast<const f32x4*>(smem + (uint32_t)q * RF + ((uint32_t)(c ^ (q & 15)) << 4));
         const int r = m0 + rbase + q;
         if (r < p.M && col < p.N)
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (int64_t)r * p.ldc + col));
       }
     };
-    constexpr int kRounds = kRound == 256 ? NB : 2;
-    StaticFor<0, kRounds>::run([&](auto r_tag) {
-      constexpr int rd = decltype(r_tag)::value;
-      constexpr int b = kRound == 256 ? rd : 0;
-      if constexpr (rd > 0) lds_barrier();
-      if (kRound == 256 || wm == rd) {
-        StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
-          constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
-          const float v[4] = {acc[b][i][j][4 * g], acc[b][i][j][4 * g + 1], acc[b][i][j][4 * g + 2],
-                              acc[b][i][j][4 * g + 3]};
-          put_f4((kRound == 256 ? wm * WM : 0) + i * 32 + (lane & 31),
-                 wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
-        });
-      }
+    StaticFor<0, NB * kRoundsPerOp>::run([&](auto r_tag) {
+      constexpr int x0 = decltype(r_tag)::value, b = x0 / kRoundsPerOp, rd = x0 % kRoundsPerOp;
+      if constexpr (x0 > 0) lds_barrier();
+      StaticFor<0, MI>::run([&](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value;
+        const int row = wm * WM + i * 32;  // first tile row of the 32-row block
+        if (row / kRows == rd) {
+          StaticFor<0, NJ * 4>::run([&](auto tag) {
+            constexpr int j = decltype(tag)::value / 4, g = decltype(tag)::value % 4;
+            const float v[4] = {acc[b][i][j][4 * g], acc[b][i][j][4 * g + 1], acc[b][i][j][4 * g + 2],
+                                acc[b][i][j][4 * g + 3]};
+            put_f4(row - rd * kRows + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+          });
+        }
+      });
       lds_barrier();
       float* C = reinterpret_cast<float*>(b ? p.C1 : p.C0) + (int64_t)e * p.sCe;
-      store_round(C, kRound == 256 ? 0 : rd * 128);
+      store_round(C, rd * kRows);
     });
   } else if constexpr (kSwapAB) {
     // transposed 32x32 result: lane l holds row (l % 32) and, for v = 4g + t,
