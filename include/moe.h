@@ -36,8 +36,16 @@
  *    MOE_ERR_UNSUPPORTED or MOE_ERR_SHAPE.  S = 0 is valid and enqueues only
  *    the work that clears outputs.
  *  - Thread safety: no mutable global state except the optional kernel timer
- *    (moe_timer_*).  Concurrent calls on different streams must use
+ *    (moe_timer_*) and idempotent per-device caches (the compute-unit count,
+ *    kernel attributes).  Concurrent calls on different streams must use
  *    different workspaces.
+ *  - Reproducibility: every reduction runs in a fixed order, so repeated
+ *    calls on the same device give bit-identical results.  The products
+ *    with a plain store epilogue (y of the expert FFN, dxd of its backward)
+ *    split the tiles of a partial last wave of GEMM tiles along K and sum
+ *    the fp32 parts in part order; the split depends on the device's
+ *    compute-unit count, so devices of another size may round those
+ *    outputs differently (fp32 summation order only).
  */
 #ifndef MOE_H_
 #define MOE_H_

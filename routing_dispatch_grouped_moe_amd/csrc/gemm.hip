@@ -8,15 +8,11 @@
 //   M-grouped  C[rows of e, N] = A[rows of e, K] * B_e[K, N]      (fwd, dA, dxd)
 //   K-grouped  C_e[M, N] = A[rows of e, M]^T * B[rows of e, N]    (dW1, dW3, dW2)
 //
-// gfx950 design.  A block of eight wavefronts (2 x 4, two per SIMD)
-// computes a 256 x 256 tile (256 x (128 + 128) for the two-operand gate/up
-// and dW1/dW3 cases), each wavefront 128 x 64 as 4 x 2 (or 4 x 1 per
-// operand) v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators; with two
-// wavefronts per SIMD one issues MFMAs while the other waits on LDS.  K
-// advances 64 per step.  Operand tiles live in LDS in one of two layouts,
-// both XOR-swizzled on 16-byte chunks for the 64-bank LDS (a ds_read_b128
-// serves 16 lanes per cycle; measured conflict-free with a bank-conflict
-// probe):
+// gfx950 design.  Every bf16 product computes 256 x 256 output tiles
+// (256 x (128 + 128) for the two-operand gate/up and dW1/dW3 cases) on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators, K advancing 64 per step.
+// Operand tiles live in LDS in one of two layouts, both XOR-swizzled on
+// 16-byte chunks for the 64-bank LDS (measured conflict-free):
 //   - K-contiguous rows ([rows][64], 128 B a row) for operands stored
 //     K-major in HBM (activations in the forward, weights in dA/dxd);
 //     fragments are read with ds_read_b128;
@@ -25,13 +21,20 @@
 //     fragments are read with the gfx950 LDS transpose load
 //     ds_read_b64_tr_b16, which hands each lane four consecutive-k values of
 //     one column, so no operand is ever transposed in registers.
-// Global reads are 16-byte buffer loads bounded to the expert's rows (reads
+// Two tile forms:
+//   - one wavefront per SIMD (gemm_bf16_w4_kernel): the forward, dA, dxd and
+//     the weight gradients of experts with many rows.  256 accumulators per
+//     lane, operands reach LDS by direct loads, and every epilogue is staged
+//     through LDS and leaves as whole rows;
+//   - eight wavefronts, two per SIMD (gemm_bf16_kernel): the weight
+//     gradients of experts with few rows and the accumulating weight
+//     gradients, with register-staged loads one K step ahead.
+// Global reads are bounded by buffer descriptors to the expert's rows (reads
 // past the end return zero, which pads ragged M tiles and the ragged K tail
-// of the weight gradients).  The next K step is loaded into registers while
-// the current one runs on MFMA; LDS is double buffered with one barrier per
-// step.  M tiles come from a device-built table (expert, first row), so
-// nothing syncs with the host; their block ids are renumbered so that each
-// XCD (own L2) runs a contiguous patch of tiles.
+// of the weight gradients).  M tiles come from a device-built table (expert,
+// first row), so nothing syncs with the host; their block ids are renumbered
+// so that each XCD (own L2) runs a contiguous patch of tiles, and the tiles
+// of a partial last wave of the plain-store products are split along K.
 //
 // The fp32 storage type (the tiny fp32 workload) uses a plain FMA kernel
 // with the same tile table and epilogues.
@@ -115,47 +118,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
     if constexpr (DUAL) {
       float* c1 = reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o;
       __builtin_nontemporal_store(EPI == EPI_F32_ACC ? *c1 + v1 : v1, c1);
-    }
-  }
-}
-
-// The same epilogues on four consecutive columns (col % 4 == 0) of one row:
-// one 8-byte bf16 or 16-byte fp32 access per operand instead of four.
-template <int EPI, bool DUAL>
-__device__ __forceinline__ void epilogue4(const GemmArgs& p, int e, int64_t row, int col,
-                                          const float (&v0)[4], const float (&v1)[4]) {
-  const int64_t o = row * p.ldc + col;
-  if constexpr (EPI == EPI_STORE) {
-    store4_bf16(p.C0, o, v0);
-  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    float a[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = silu_f(v0[t]) * v1[t];
-    store4_bf16(p.C0, o, v0);
-    store4_bf16(p.C1, o, v1);
-    store4_bf16(p.C2, o, a);
-  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    float z[4], u[4], d1[4], d3[4];
-    load4_bf16(p.X0, o, z);
-    load4_bf16(p.X1, o, u);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float sg = sigmoid_f(z[t]);
-      d1[t] = v0[t] * u[t] * sg * (1.0f + z[t] * (1.0f - sg));
-      d3[t] = v0[t] * z[t] * sg;
-    }
-    store4_bf16(p.C0, o, d1);
-    store4_bf16(p.C1, o, d3);
-  } else {
-    float4* c0 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C0) + (int64_t)e * p.sCe + o);
-    float4 w0 = make_float4(v0[0], v0[1], v0[2], v0[3]);
-    if (EPI == EPI_F32_ACC) { const float4 q = *c0; w0.x += q.x; w0.y += q.y; w0.z += q.z; w0.w += q.w; }
-    *c0 = w0;
-    if constexpr (DUAL) {
-      float4* c1 = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C1) + (int64_t)e * p.sCe + o);
-      float4 w1 = make_float4(v1[0], v1[1], v1[2], v1[3]);
-      if (EPI == EPI_F32_ACC) { const float4 q = *c1; w1.x += q.x; w1.y += q.y; w1.z += q.z; w1.w += q.w; }
-      *c1 = w1;
     }
   }
 }
@@ -405,11 +367,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
-  // The transposed MFMA result (four consecutive columns per lane) for every
-  // kind but the accumulating weight gradient, which keeps the direct one
-  // (each 4-byte store instruction covers two whole 128-byte rows).  The
-  // overwriting weight gradient is staged through LDS and leaves as whole
-  // rows.
+  // This form serves the fp32 weight gradients only.  The overwriting kind
+  // takes the transposed MFMA result (four consecutive columns per lane),
+  // staged through LDS and stored as whole rows; the accumulating kind keeps
+  // the direct result (each 4-byte load/store instruction covers two whole
+  // 128-byte rows of the gradient it adds to).
+  static_assert(epi_f32(EPI), "the eight-wavefront form computes fp32 weight gradients");
   constexpr bool kSwapAB = EPI != EPI_F32_ACC;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -589,26 +552,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       lds_barrier();
       float* C = reinterpret_cast<float*>(b ? p.C1 : p.C0) + (int64_t)e * p.sCe;
       store_round(C, rd * kRows);
-    });
-  } else if constexpr (kSwapAB) {
-    // transposed 32x32 result: lane l holds row (l % 32) and, for v = 4g + t,
-    // column 8 g + 4 (l / 32) + t
-StaticFor<0, MI>::run([&](auto i_tag) {
-      constexpr int i = decltype(i_tag)::value;
-      const int r = wm * WM + i * 32 + (lane & 31);
-      const bool row_ok = KGROUP ? (m0 + r < p.M) : (r < valid);
-      const int64_t grow = KGROUP ? (int64_t)(m0 + r) : row0 + r;
-      StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
-        constexpr int j = decltype(jg_tag)::value / 4, g = decltype(jg_tag)::value % 4;
-        const int c = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        float v0[4], v1[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v0[t] = acc[0][i][j][4 * g + t];
-          v1[t] = DUAL ? acc[NB - 1][i][j][4 * g + t] : 0.f;
-        }
-        if (row_ok && c < p.N) epilogue4<EPI, DUAL>(p, e, grow, c, v0, v1);
-      });
     });
   } else {
     // direct 32x32 result: lane holds column (lane % 32), rows 8 (v/4) + 4 (lane/32) + v%4

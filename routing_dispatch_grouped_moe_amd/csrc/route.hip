@@ -5,15 +5,15 @@
 // routing sparse).
 //
 // gfx950 design: a block owns 32 tokens.  The router GEMM runs on MFMA
-// (v_mfma_f32_16x16x32_bf16) with both operands read straight from global
-// memory in K-contiguous 16-byte fragments: x rows as they are, and the
-// router weight through a transposed copy WgT [Epad, H] made once per call.
-// Waves split the expert columns, or the H reduction when there are fewer
-// than four 16-wide column blocks; partial sums meet in LDS in a fixed order.
-// Top-K then runs one token per wavefront: each lane holds E/64 64-bit order
-// keys (ordered logit bits : ~expert), and K rounds of a butterfly max pick
-// the winners.  Counts come from an LDS histogram flushed with one atomic
-// per (block, expert).
+// (v_mfma_f32_16x16x32_bf16) against a transposed copy of the router weight,
+// WgT [Epad, H], made once per call; both operands stream through a ring of
+// LDS stages filled by direct global->LDS loads, several K slices ahead of
+// the MFMAs.  Waves split the 16-expert column blocks, or the H reduction
+// when there are fewer than four column blocks (partial sums meet in LDS in
+// a fixed order).  Top-K then runs one token per wavefront: each lane holds
+// E/64 64-bit order keys (ordered logit bits : ~expert), and K rounds of a
+// butterfly max pick the winners.  Counts come from an LDS histogram flushed
+// with one atomic per (block, expert).
 #include <algorithm>
 
 #include "dev_common.h"
