@@ -122,33 +122,38 @@ __device__ __forceinline__ int xswz(int r) {
   return CPR == 4 ? (r >> 2) & 3 : CPR == 8 ? (r >> 1) & 7 : r & 15;
 }
 
-// Bias, logits, softmax, top-K and counts of the block's tokens from the
-// partial logits part[ks][32][epad] (summed in slice order).
-__device__ __forceinline__ void route_tail(float* part, int* hist, int ks, const float* bias,
-                                           float* logits, int32_t* idx, float* gates,
-                                           int32_t* counts, uint32_t* status, int t0, int nt,
-                                           int E, int epad, int K, int renorm) {
+// Logits, softmax, top-K and counts of the block's tokens from the partial
+// logits part[ks][32][epad] (the bias already in slice 0; slices summed in
+// slice order).  Wavefront w owns tokens w, w + 4, ...: it finishes their
+// logit rows (coalesced row stores, no index division) and then picks
+// their top K.  NJ bounds the keys per lane (E <= 64 NJ).
+template <int NJ>
+__device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float* logits,
+                                           int32_t* idx, float* gates, int32_t* counts,
+                                           uint32_t* status, int t0, int nt, int E, int epad,
+                                           int K, int renorm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   uint32_t bad = 0;
-  for (int i = tid; i < nt * E; i += 256) {
-    const int t = i / E, e = i % E;
-    float v = part[t * epad + e];
-    for (int k2 = 1; k2 < ks; ++k2) v += part[((size_t)k2 * kRouteBT + t) * epad + e];
-    if (bias) v += bias[e];
-    part[t * epad + e] = v;
-    if (!isfinite(v)) bad = 1;
-    if (logits) logits[(int64_t)(t0 + t) * E + e] = v;
+  for (int t = w; t < nt; t += 4) {
+    float* lrow = part + t * epad;
+    for (int e = lane; e < E; e += 64) {
+      float v = lrow[e];
+      for (int k2 = 1; k2 < ks; ++k2) v += part[((size_t)k2 * kRouteBT + t) * epad + e];
+      if (ks > 1) lrow[e] = v;
+      if (!isfinite(v)) bad = 1;
+      if (logits) logits[(int64_t)(t0 + t) * E + e] = v;
+    }
   }
   if (bad) atomicOr(status, (uint32_t)MOE_DEV_NONFINITE_LOGIT);
-  __syncthreads();
 
-  // Top-K: one token per wavefront.
+  // Top-K: one token per wavefront at a time (the rows this wavefront just
+  // finished, so no barrier is needed).
   const int nj = (E + 63) / 64;
   for (int t = w; t < nt; t += 4) {
     const float* lrow = part + t * epad;
-    uint64_t keys[16];
+    uint64_t keys[NJ];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       keys[j] = (j < nj && e < E) ? topk_key(lrow[e], e) : 0ull;
     }
@@ -157,10 +162,10 @@ __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, const
     for (int k = 0; k < K; ++k) {
       uint64_t best = 0ull;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) best = keys[j] > best ? keys[j] : best;
+      for (int j = 0; j < NJ; ++j) best = keys[j] > best ? keys[j] : best;
       best = wave_max_u64(best);
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (keys[j] == best) keys[j] = 0ull;
       const int e = key_expert(best);
       const float l = lrow[e];
@@ -290,22 +295,26 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
   // every direct load has landed and every wavefront is done with the stages
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // 16x16 MFMA result: lane holds column (lane % 16), rows 4 (lane / 16) + i
+  // 16x16 MFMA result: lane holds column (lane % 16), rows 4 (lane / 16) + i;
+  // slice 0 carries the bias
   float* part = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int nbk = wn + cb * NWN;
     if (nbk * 16 < epad) {
       const int col = nbk * 16 + r16;
+      const float bv = (bias != nullptr && ksi == 0 && col < E) ? bias[col] : 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          part[((size_t)ksi * kRouteBT + rb * 16 + q * 4 + i) * epad + col] = acc[rb][cb][i];
+          part[((size_t)ksi * kRouteBT + rb * 16 + q * 4 + i) * epad + col] = acc[rb][cb][i] + bv;
     }
   }
   __syncthreads();
-  route_tail(part, hist, KS, bias, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
+  // keys per lane: at most NCB (one wavefront row of K) or one (E < 64)
+  route_tail<KS == 1 ? NCB : 1>(part, hist, KS, logits, idx, gates, counts, status, t0, nt, E,
+                                epad, K, renorm);
 }
 
 // fp32 router: plain dot products, one (token, expert) pair per thread.
@@ -332,10 +341,10 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
       const float* wr = wgT + (int64_t)e * H;
       for (int h = 0; h < H; ++h) acc = fmaf(xr[h], wr[h], acc);
     }
-    fpart[t * epad + e] = acc;
+    fpart[t * epad + e] = acc + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
-  route_tail(fpart, hist, 1, bias, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
+  route_tail<16>(fpart, hist, 1, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
 }
 
 template <int NCB, int KS, int U>
