@@ -37,27 +37,53 @@ __global__ __launch_bounds__(256) void mod_score_kernel(const void* __restrict__
   if (lane == 0) r[s] = acc;
 }
 
-// One block (1024 threads) per sequence; T <= 8192.
+// One block (1024 threads) per sequence; T <= 8192.  The (score, position)
+// keys are unique (ties broken toward the earlier position), so the kept set
+// is the C largest keys: a bitonic sort of the keys in LDS (descending,
+// padded to a power of two with zero keys, which sort last), then the top C
+// positions are marked in a bitmap and written out in position order
+// through a block scan of per-thread counts.
 __global__ __launch_bounds__(1024) void mod_select_kernel(const float* __restrict__ r,
                                                           int32_t* __restrict__ keep, int T,
                                                           int C) {
   __shared__ uint64_t keys[8192];
+  __shared__ uint32_t kept[8192 / 32];
   __shared__ int scan[1024];
   const int b = blockIdx.x, tid = threadIdx.x;
-  for (int t = tid; t < T; t += 1024) keys[t] = topk_key(r[(int64_t)b * T + t], t);
+  int N = 1;
+  while (N < T) N <<= 1;
+  for (int t = tid; t < N; t += 1024) keys[t] = t < T ? topk_key(r[(int64_t)b * T + t], t) : 0ull;
+  for (int i = tid; i < 8192 / 32; i += 1024) kept[i] = 0u;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int x = tid; x < N; x += 1024) {
+        const int y = x ^ j;
+        if (y > x) {
+          const uint64_t kx = keys[x], ky = keys[y];
+          // blocks with (x & k) == 0 end descending, the others ascending,
+          // so the final merge leaves the whole array descending
+          if (((x & k) == 0) ? (kx < ky) : (kx > ky)) {
+            keys[x] = ky;
+            keys[y] = kx;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < C; i += 1024) {
+    const int t = key_expert(keys[i]);  // the position stored in the key's low word
+    atomicOr(&kept[t >> 5], 1u << (t & 31));
+  }
   __syncthreads();
   // Each thread owns a run of consecutive positions.
   const int per = (T + 1023) / 1024;
   const int t0 = tid * per;
-  uint32_t flags = 0;  // bit i: position t0 + i kept (per <= 8)
   int cnt = 0;
   for (int i = 0; i < per; ++i) {
     const int t = t0 + i;
-    if (t >= T) break;
-    const uint64_t k = keys[t];
-    int rank = 0;
-    for (int u = 0; u < T; ++u) rank += keys[u] > k ? 1 : 0;
-    if (rank < C) { flags |= 1u << i; ++cnt; }
+    if (t < T && (kept[t >> 5] >> (t & 31)) & 1u) ++cnt;
   }
   scan[tid] = cnt;
   __syncthreads();
@@ -68,8 +94,10 @@ __global__ __launch_bounds__(1024) void mod_select_kernel(const float* __restric
     __syncthreads();
   }
   int j = scan[tid] - cnt;
-  for (int i = 0; i < per; ++i)
-    if (flags & (1u << i)) keep[(int64_t)b * C + j++] = b * T + t0 + i;
+  for (int i = 0; i < per; ++i) {
+    const int t = t0 + i;
+    if (t < T && (kept[t >> 5] >> (t & 31)) & 1u) keep[(int64_t)b * C + j++] = b * T + t;
+  }
 }
 
 // Copy rows: dst[j] = src[idx[j]] (one wavefront per row).
