@@ -66,11 +66,7 @@ __device__ __forceinline__ void store1(void* base, int64_t elem, float v) {
   else reinterpret_cast<float*>(base)[elem] = v;
 }
 
-// Four consecutive bf16 elements (8 bytes, 8-byte aligned) as fp32.
-__device__ __forceinline__ void load4_bf16(const void* base, int64_t elem, float (&v)[4]) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + elem);
-  v[0] = bf16_lo(w[0]); v[1] = bf16_hi(w[0]); v[2] = bf16_lo(w[1]); v[3] = bf16_hi(w[1]);
-}
+// Four fp32 values as four consecutive bf16 elements (8 bytes, 8-byte aligned).
 __device__ __forceinline__ void store4_bf16(void* base, int64_t elem, const float (&v)[4]) {
   u32x2 w;
   w[0] = pack_bf16x2(v[0], v[1]);
