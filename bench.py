@@ -126,7 +126,20 @@ def cpu_baseline(name, maxvio, sample_tokens):
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of the {wl.S_in} tokens of {cfg['workload']} (E={E}, H={H}, "
                       f"H'={Hf}), host-drawn weights of the same distribution, float64 "
-                      f"forward+backward incl. weight gradients, {t:.1f} s"}
+                      f"forward+backward incl. weight gradients, {t:.1f} s",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """CPU model name of the host, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -232,7 +245,7 @@ def main():
         rl = roofline_entry(name, mcfg, counts, avg, bf16)
         if rl:
             ent.update({"bound": rl["bound"], "frac": rl["frac"], "achieved": rl["achieved"],
-                        "unit": rl["unit"]})
+                        "unit": rl["unit"], "flops": rl["flops"], "bytes": rl["bytes"]})
         kernels[name] = ent
     dom = max(kernels, key=lambda k: kernels[k]["total_ms_per_step"])
     dom_avg = kernels[dom]["avg_us"] / 1e6
@@ -269,6 +282,12 @@ def main():
         "dispatch_hbm_frac": disp.get("frac") if disp.get("bound") == "hbm" else None,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "kernels_frac": {k: round(v["frac"], 4) for k, v in kernels.items() if "frac" in v},
+        # both fractions of every modelled kernel: algorithmic FLOPs against the
+        # bf16 MFMA peak and algorithmic bytes against the HBM peak
+        "kernels_mfma_hbm_frac": {
+            k: [round(v["flops"] / (v["avg_us"] * 1e-6) / PEAK_BF16, 4),
+                round(v["bytes"] / (v["avg_us"] * 1e-6) / PEAK_HBM, 4)]
+            for k, v in kernels.items() if "flops" in v and v["avg_us"] > 0},
     }
     if not args.no_cpu_baseline:
         del x, Wg, dout, W1, W3, W2, layer, moe
