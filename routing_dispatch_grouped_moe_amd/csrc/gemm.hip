@@ -542,14 +542,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
           f32x4{v[0], v[1], v[2], v[3]};
     };
     auto store_round = [&](float* C, int rbase) __attribute__((always_inline)) {
-      const int c = lane % LPRF, col = n0 + 4 * c;
+      // lane (c, q0) stores chunk c of rows q0, q0 + kPass, ...: one row
+      // pointer per lane advanced by a fixed stride, one row-count compare
+      constexpr int kPass = kWaves * RPIF;
+      const int c = lane % LPRF, col = n0 + 4 * c, q0 = w * RPIF + lane / LPRF;
+      if (col >= p.N) return;
+      const int left = p.M - (m0 + rbase + q0);
+      float* dst = C + (int64_t)(m0 + rbase + q0) * p.ldc + col;
+      const int64_t step = (int64_t)kPass * p.ldc;
+      const char* src = smem + (uint32_t)q0 * RF;
 #pragma unroll
-      for (int it = 0; it < kRows / (kWaves * RPIF); ++it) {
-        const int q = (it * kWaves + w) * RPIF + lane / LPRF;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + (uint32_t)q * RF + ((uint32_t)(c ^ (q & 15)) << 4));
-        const int r = m0 + rbase + q;
-        if (r < p.M && col < p.N)
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (int64_t)r * p.ldc + col));
+      for (int it = 0; it < kRows / kPass; ++it) {
+        const int q = q0 + it * kPass;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + it * kPass * RF + ((uint32_t)(c ^ (q & 15)) << 4));
+        if (it * kPass < left) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+        dst += step;
       }
     };
     StaticFor<0, NB * kRoundsPerOp>::run([&](auto r_tag) {
@@ -934,24 +941,34 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
       const u32x2 w2 = *reinterpret_cast<const u32x2*>(st + o);
       v[0] = bf16_lo(w2[0]); v[1] = bf16_hi(w2[0]); v[2] = bf16_lo(w2[1]); v[3] = bf16_hi(w2[1]);
     };
-    // NR staged rows -> memory; staged row q is tile row rowmap(q).  Each
-    // instruction of the block covers RPI whole rows; wavefront w takes every
-    // fourth one.
-    auto store_rows = [&](const char* st, auto nr_tag, void* C, auto rowmap) {
-      constexpr int NR = decltype(nr_tag)::value;
-      const int c = lane % LPR, col = n0 + 8 * c;
+    // NR staged rows -> memory; staged row q is tile row
+    // rbase + q + (q / SEG) * GAP (runs of SEG rows, GAP rows apart).  Each
+    // instruction of the block covers RPI whole rows (kPass rows a pass of
+    // the four wavefronts); lane (c, q0) stores chunk c of staged rows
+    // q0, q0 + kPass, ... through one row pointer, the row offsets being
+    // compile-time multiples of ldc.
+    auto store_rows = [&](const char* st, auto nr_tag, void* C, int rbase, auto seg_tag, auto gap_tag) {
+      constexpr int NR = decltype(nr_tag)::value, SEG = decltype(seg_tag)::value,
+                    GAP = decltype(gap_tag)::value, kPass = 4 * RPI;
+      static_assert(NR % kPass == 0 && SEG % kPass == 0, "staged row passes");
+      const int c = lane % LPR, col = n0 + 8 * c, q0 = w * RPI + lane / LPR;
+      if (col >= p.N) return;
+      const int left = valid - (rbase + q0);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(C) + (row0 + rbase + q0) * p.ldc + col;
+      const char* src = st + (uint32_t)q0 * RS;
 #pragma unroll
-      for (int it = 0; it < NR / (4 * RPI); ++it) {
-        const int q = (it * 4 + w) * RPI + lane / LPR;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + (uint32_t)q * RS + ((uint32_t)(c ^ (q & 15)) << 4));
-        const int r = rowmap(q);
-        if (r < valid && col < p.N)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + (row0 + r) * p.ldc + col) = v;
+      for (int it = 0; it < NR / kPass; ++it) {
+        const int qd = it * kPass, rd = qd + (qd / SEG) * GAP;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + qd * RS + ((uint32_t)(c ^ ((q0 + qd) & 15)) << 4));
+        if (rd < left) *reinterpret_cast<u32x4*>(dst + (int64_t)rd * p.ldc) = v;
       }
     };
     using R128 = std::integral_constant<int, 128>;
     using R256 = std::integral_constant<int, 256>;
     using R64 = std::integral_constant<int, 64>;
+    using R32 = std::integral_constant<int, 32>;
+    using R96 = std::integral_constant<int, 96>;
+    using R0 = std::integral_constant<int, 0>;
 
     if constexpr (EPI == EPI_F32) {
       // fp32 weight gradient of expert e (K-grouped): rows of BN floats
@@ -971,16 +988,23 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         *reinterpret_cast<f32x4*>(st + o) = f32x4{v[0], v[1], v[2], v[3]};
       };
       auto store_round = [&](float* C, int rbase) __attribute__((always_inline)) {
-        const int c = lane % LPRF, col = n0 + 4 * c;
+        // lane (c, q0) stores chunk c of staged rows q0, q0 + kPass, ...
+        // through one row pointer advanced by kPass rows
+        constexpr int kPass = 4 * RPIF;
+        static_assert(kHalfRows % kPass == 0, "staged row passes");
+        const int c = lane % LPRF, col = n0 + 4 * c, q0 = w * RPIF + lane / LPRF;
+        if (col >= p.N) return;
+        const int left = p.M - (m0 + rbase + q0);
+        float* dst = C + (int64_t)(m0 + rbase + q0) * p.ldc + col;
+        const int64_t step = (int64_t)kPass * p.ldc;
 #pragma unroll
-        for (int it = 0; it < kRound / (4 * RPIF); ++it) {
-          const int q = (it * 4 + w) * RPIF + lane / LPRF;
-          const char* st = q < kHalfRows ? stage0 : stage1;
-          const int ql = q < kHalfRows ? q : q - kHalfRows;
+        for (int it = 0; it < kRound / kPass; ++it) {
+          const int qd = it * kPass;
+          const char* st = qd < kHalfRows ? stage0 : stage1;
+          const int ql = q0 + (qd < kHalfRows ? qd : qd - kHalfRows);
           const f32x4 v = *reinterpret_cast<const f32x4*>(st + (uint32_t)ql * RF + ((uint32_t)(c ^ (ql & 15)) << 4));
-          const int r = m0 + rbase + q;
-          if (r < p.M && col < p.N)
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (int64_t)r * p.ldc + col));
+          if (qd < left) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+          dst += step;
         }
       };
       if constexpr (kRound == 256) {
@@ -1027,8 +1051,8 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         put4(st, i * 32 + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
       });
       __syncthreads();
-      store_rows(stage0, R128{}, p.C0, [](int q) { return q; });
-      store_rows(stage1, R128{}, p.C0, [](int q) { return q + 128; });
+      store_rows(stage0, R128{}, p.C0, 0, R128{}, R0{});
+      store_rows(stage1, R128{}, p.C0, 128, R128{}, R0{});
     } else if constexpr (EPI == EPI_SWIGLU_FWD) {
       // h1 in stage 0 and a = silu(h1) h3 in stage 1 (256 rows x 128 columns
       // each; a from the fp32 accumulators), then h3 in stage 0
@@ -1046,8 +1070,8 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         put4(stage1, r, c, a);
       });
       __syncthreads();
-      store_rows(stage0, R256{}, p.C0, [](int q) { return q; });
-      store_rows(stage1, R256{}, p.C2, [](int q) { return q; });
+      store_rows(stage0, R256{}, p.C0, 0, R256{}, R0{});
+      store_rows(stage1, R256{}, p.C2, 0, R256{}, R0{});
       __syncthreads();
       StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
         constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
@@ -1057,7 +1081,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         put4(stage0, r, c, v1);
       });
       __syncthreads();
-      store_rows(stage0, R256{}, p.C1, [](int q) { return q; });
+      store_rows(stage0, R256{}, p.C1, 0, R256{}, R0{});
     } else {
       // SwiGLU backward: four phases, one per 32-row group i of both
       // wavefront rows (64 tile rows).  A phase's h1 and h3 rows (32 KB each)
@@ -1069,18 +1093,26 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
       constexpr int kLd = 2 * 64 * LPR / kThreads4;    // 16-byte loads per lane per phase
       const uint16_t* h1 = reinterpret_cast<const uint16_t*>(p.X0);
       const uint16_t* h3 = reinterpret_cast<const uint16_t*>(p.X1);
-      // staged row q of a phase holds tile row (q / 32) * 128 + 32 i + q % 32
-      auto tile_row = [](int i, int q) { return (q >> 5) * 128 + i * 32 + (q & 31); };
+      // staged row q of a phase holds tile row (q / 32) * 128 + 32 i + q % 32.
+      // 16-byte piece u * kThreads4 + tid of a phase: matrix u / (kLd / 2),
+      // staged row q0 + kStep (u % (kLd / 2)), chunk tid % LPR.
+      constexpr int kStep = kThreads4 / LPR;
+      static_assert(kThreads4 % LPR == 0 && (kLd / 2) * kStep == 64 && 32 % kStep == 0, "phase pieces");
+      const int q0 = tid / LPR;
+      const int64_t cofs = min(n0 + 8 * (tid % LPR), p.N - 8);
+      const uint16_t* z1 = h1 + row0 * p.ldc + cofs;   // row 0 of the tile
+      const uint16_t* z3 = h3 + row0 * p.ldc + cofs;
+      const int64_t oq0 = (int64_t)q0 * p.ldc;
       u32x4 pre[kLd];
       auto load_phase = [&](int i) {
 #pragma unroll
         for (int u = 0; u < kLd; ++u) {
-          const int f = u * kThreads4 + tid;           // 16-byte piece of the phase
-          const int m = f / (64 * LPR), q = (f / LPR) % 64, c = f % LPR;
+          const int qd = kStep * (u % (kLd / 2));
+          const int rd = 32 * i + qd + (qd / 32) * 96;   // tile row minus q0
           // rows past the tile's valid ones read row 0 (never stored)
-          const int r = tile_row(i, q);
-          const int64_t o = (row0 + (r < valid ? r : 0)) * p.ldc + min(n0 + 8 * c, p.N - 8);
-          pre[u] = *reinterpret_cast<const u32x4*>((m ? h3 : h1) + o);
+          const uint16_t* z = u < kLd / 2 ? z1 : z3;
+          const uint16_t* src = rd + q0 < valid ? z + oq0 + (int64_t)rd * p.ldc : z;
+          pre[u] = *reinterpret_cast<const u32x4*>(src);
         }
       };
       auto put_phase = [&](char* st) {
@@ -1117,8 +1149,8 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
           put4(st + kHalfB, q, c, d3);
         });
         __syncthreads();
-        store_rows(st, R64{}, p.C0, [&](int qq) { return tile_row(i, qq); });
-        store_rows(st + kHalfB, R64{}, p.C1, [&](int qq) { return tile_row(i, qq); });
+        store_rows(st, R64{}, p.C0, 32 * i, R32{}, R96{});
+        store_rows(st + kHalfB, R64{}, p.C1, 32 * i, R32{}, R96{});
         if constexpr (i + 1 < MI) put_phase((i & 1) ? stage0 : stage1);
       });
     }
