@@ -114,18 +114,49 @@ __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, const vo
 }
 
 // ------------------------------------------------------- wave reductions --
+// Cross-lane steps on DPP (VALU lane moves, no LDS round trip): butterfly
+// within each 16-lane row (quad swaps, then the half-row and row mirrors),
+// then the rows combined through the broadcasts of lanes 15 and 31, so that
+// lane 63 holds the reduction of the whole wavefront; it is then read out
+// to every lane.  Lanes of rows a step leaves out get `old`.  The whole
+// wavefront must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __uint_as_float(dpp_mov<CTRL, ROWS>(0u, __float_as_uint(v)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v = dpp_add<kDppXor1, 0xf>(v);
+  v = dpp_add<kDppXor2, 0xf>(v);
+  v = dpp_add<kDppHalfMirror, 0xf>(v);
+  v = dpp_add<kDppMirror, 0xf>(v);
+  v = dpp_add<kDppBcast15, 0xa>(v);
+  v = dpp_add<kDppBcast31, 0xc>(v);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint64_t o = ((uint64_t)dpp_mov<CTRL, ROWS>(hi, hi) << 32) | dpp_mov<CTRL, ROWS>(lo, lo);
+  return o > v ? o : v;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  v = dpp_max<kDppXor1, 0xf>(v);
+  v = dpp_max<kDppXor2, 0xf>(v);
+  v = dpp_max<kDppHalfMirror, 0xf>(v);
+  v = dpp_max<kDppMirror, 0xf>(v);
+  v = dpp_max<kDppBcast15, 0xa>(v);
+  v = dpp_max<kDppBcast31, 0xc>(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---------------------------------------------------- top-K order keys --

@@ -8,9 +8,12 @@
 // (v_mfma_f32_16x16x32_bf16) against a transposed copy of the router weight,
 // WgT [Epad, H], made once per call; both operands stream through a ring of
 // LDS stages filled by direct global->LDS loads, several K slices ahead of
-// the MFMAs.  Waves split the 16-expert column blocks, or the H reduction
-// when there are fewer than four column blocks (partial sums meet in LDS in
-// a fixed order).  Top-K then runs one token per wavefront: each lane holds
+// the MFMAs.  Four wavefronts issue those loads and four others read the
+// stages and run the MFMAs, so a stall of the address unit never holds up
+// the matrix core.  The MFMA wavefronts split the 16-expert column blocks,
+// or the H reduction when there are fewer than four column blocks (partial
+// sums meet in LDS in a fixed order).  Top-K then runs one token per
+// wavefront on all eight: each lane holds
 // E/64 64-bit order keys (ordered logit bits : ~expert), and K rounds of a
 // butterfly max pick the winners.  Counts come from an LDS histogram flushed
 // with one atomic per (block, expert).
@@ -23,6 +26,7 @@
 namespace moe {
 
 constexpr int kRouteBT = 32;
+constexpr int kRouteWaves = 8;  // bf16 router: 4 load wavefronts + 4 MFMA wavefronts
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -124,17 +128,17 @@ __device__ __forceinline__ int xswz(int r) {
 
 // Logits, softmax, top-K and counts of the block's tokens from the partial
 // logits part[ks][32][epad] (the bias already in slice 0; slices summed in
-// slice order).  Wavefront w owns tokens w, w + 4, ...: it finishes their
+// slice order).  Wavefront w of NW owns tokens w, w + NW, ...: it finishes their
 // logit rows (coalesced row stores, no index division) and then picks
 // their top K.  NJ bounds the keys per lane (E <= 64 NJ).
-template <int NJ>
+template <int NJ, int NW>
 __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float* logits,
                                            int32_t* idx, float* gates, int32_t* counts,
                                            uint32_t* status, int t0, int nt, int E, int epad,
                                            int K, int renorm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   uint32_t bad = 0;
-  for (int t = w; t < nt; t += 4) {
+  for (int t = w; t < nt; t += NW) {
     float* lrow = part + t * epad;
     for (int e = lane; e < E; e += 64) {
       float v = lrow[e];
@@ -149,7 +153,7 @@ __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float
   // Top-K: one token per wavefront at a time (the rows this wavefront just
   // finished, so no barrier is needed).
   const int nj = (E + 63) / 64;
-  for (int t = w; t < nt; t += 4) {
+  for (int t = w; t < nt; t += NW) {
     const float* lrow = part + t * epad;
     uint64_t keys[NJ];
 #pragma unroll
@@ -192,7 +196,7 @@ __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256)
+  for (int e = tid; e < E; e += 64 * NW)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
@@ -200,7 +204,7 @@ __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float
 // v_mfma_f32_16x16x32_bf16, both operands streamed through an NS-stage LDS
 // ring by direct loads; NS - 1 stages are in flight while one is computed.
 template <int NCB, int KS, int U>
-__global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict__ x,
+__global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void* __restrict__ x,
                                                          const void* __restrict__ wgT,
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ logits,
@@ -215,11 +219,14 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // stages, then partial logits
   __shared__ int hist[1024];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wavefronts 0-3 compute, 4-7 load on behalf of compute wavefront w
+  const bool loader = wv >= 4;
+  const int w = wv & 3;
   const int wn = w % NWN, ksi = w / NWN;
   const int t0 = blockIdx.x * kRouteBT;
   const int nt = min(kRouteBT, S - t0);
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  for (int e = tid; e < E; e += 64 * kRouteWaves) hist[e] = 0;
 
   // per-lane byte offsets of this wavefront's direct loads (relative to the
   // stage's K origin)
@@ -259,14 +266,21 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[0][cb] = acc[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = H / T::BK;
+  if (loader) {
 #pragma unroll
-  for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
+    for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
+  }
   const int r16 = lane & 15, q = lane >> 4;
   for (int kt = 0; kt < nsteps; ++kt) {
-    // this wavefront's loads of slice kt landed; after the barrier so have
-    // everyone's, and every wavefront is done with slice kt - 1's stage
+    // a loader's loads of slice kt landed (compute wavefronts have none in
+    // flight); after the barrier so have everyone's, and every compute
+    // wavefront is done with slice kt - 1's stage, which the loads of slice
+    // kt + NS - 1 now refill
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((T::NS - 2) * T::kNI) : "memory");
-    issue(kt + T::NS - 1, (kt + T::NS - 1) % T::NS);
+    if (loader) {
+      issue(kt + T::NS - 1, (kt + T::NS - 1) % T::NS);
+      continue;
+    }
     const char* sb = smem + (kt % T::NS) * T::kStage;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int nbk = wn + cb * NWN;
-    if (nbk * 16 < epad) {
+    if (!loader && nbk * 16 < epad) {
       const int col = nbk * 16 + r16;
       const float bv = (bias != nullptr && ksi == 0 && col < E) ? bias[col] : 0.f;
 #pragma unroll
@@ -313,8 +327,8 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
   }
   __syncthreads();
   // keys per lane: at most NCB (one wavefront row of K) or one (E < 64)
-  route_tail<KS == 1 ? NCB : 1>(part, hist, KS, logits, idx, gates, counts, status, t0, nt, E,
-                                epad, K, renorm);
+  route_tail<KS == 1 ? NCB : 1, kRouteWaves>(part, hist, KS, logits, idx, gates, counts, status,
+                                             t0, nt, E, epad, K, renorm);
 }
 
 // fp32 router: plain dot products, one (token, expert) pair per thread.
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
     fpart[t * epad + e] = acc + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
-  route_tail<16>(fpart, hist, 1, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
+  route_tail<16, 4>(fpart, hist, 1, logits, idx, gates, counts, status, t0, nt, E, epad, K, renorm);
 }
 
 template <int NCB, int KS, int U>
@@ -361,7 +375,7 @@ static void route_launch_t(const void* x, const void* wgT, const float* bias, fl
                                hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
   const int blocks = (int)((S + kRouteBT - 1) / kRouteBT);
   TimedLaunch tl("route", s);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, s, x, wgT, bias, logits, idx, gates,
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kRouteWaves), lds, s, x, wgT, bias, logits, idx, gates,
                      counts, status, (int)S, H, E, epad, K, renorm ? 1 : 0);
 }
 
