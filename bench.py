@@ -4,7 +4,9 @@ One step = route -> dispatch -> grouped SwiGLU FFN (up, down) -> combine ->
 full backward (combine/gate backward, dA, dW2, dxd, dW1/dW3, dispatch and
 router backward) on one batch of synthetic tokens already resident in HBM.
 Prints ONE JSON line.  Default workload: the Mixtral-style layer
-(batch 4 x seq 2048 = 8192 tokens, H=4096, H'=14336, E=8, K=2, bf16).
+(batch 4 x seq 2048 = 8192 tokens, H=4096, H'=14336, E=8, K=2, bf16).  The
+decode-shape workload (--config c6: 128 tokens of the 384-expert layer) is
+timed forward only.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/sec fwd+bwd; grouped-GEMM % MFMA peak; dispatch % HBM BW"
+METRIC_FWD = "MoE layer tokens/sec fwd (decode shape); grouped-GEMM % HBM BW"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s dense bf16 MFMA
 PEAK_F32_VALU = 157.3e12   # FLOP/s fp32 vector
@@ -87,7 +90,7 @@ def measured_traffic(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(name, maxvio, sample_tokens):
+def cpu_baseline(name, maxvio, sample_tokens, forward_only=False):
     """Time the float64 oracle (as it stands) on a bounded token sample of the same workload."""
     import numpy as np
     import oracle
@@ -119,14 +122,16 @@ def cpu_baseline(name, maxvio, sample_tokens):
         W1(int(e))  # draws all three of expert e's matrices
     t0 = time.perf_counter()
     fw = oracle.moe_forward(x, wl.Wg, wl.bias, W1, W3, W2, wl.K)
-    bw = oracle.moe_backward(fw, dout, x, wl.Wg, W1, W3, W2, wl.K,
-                             on_dW=lambda e, g1, g3, g2: None)
+    if not forward_only:
+        oracle.moe_backward(fw, dout, x, wl.Wg, W1, W3, W2, wl.K,
+                            on_dW=lambda e, g1, g3, g2: None)
     t = time.perf_counter() - t0
-    del fw, bw
+    del fw
+    what = "forward" if forward_only else "forward+backward incl. weight gradients"
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of the {wl.S_in} tokens of {cfg['workload']} (E={E}, H={H}, "
                       f"H'={Hf}), host-drawn weights of the same distribution, float64 "
-                      f"forward+backward incl. weight gradients, {t:.1f} s",
+                      f"{what}, {t:.1f} s",
             "cpu_model": cpu_model()}
 
 
@@ -147,7 +152,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c6"])
     ap.add_argument("--maxvio", type=float, default=None, help="c4 load skew level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
@@ -173,7 +178,7 @@ def main():
     wl = make_workload(args.config, maxvio=args.maxvio, host_weights=False)
     cfg = wl.cfg
     bf16 = wl.dtype == "bf16"
-    tdt = torch.bfloat16 if bf16 else torch.float32
+    fwd_only = bool(cfg.get("forward_only"))
 
     def up(a):
         from synth import bf16_bits
@@ -200,7 +205,8 @@ def main():
 
         def step():
             layer.forward(x, Wg, bias, W1, W3, W2)
-            layer.backward(dout, x, Wg, W1, W3, W2)
+            if not fwd_only:
+                layer.backward(dout, x, Wg, W1, W3, W2)
 
     def say(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -256,13 +262,13 @@ def main():
             "algorithmic_flops": rl.get("flops"), "algorithmic_bytes": rl.get("bytes")}
 
     gemm_names = ["ffn_up", "ffn_down", "bwd_dA", "bwd_dW2", "bwd_dxd", "bwd_dW13"]
-    gflops = sum(kernel_model(n, mcfg, counts)[0] for n in gemm_names)
+    gflops = sum(kernel_model(n, mcfg, counts)[0] for n in gemm_names if n in kernels)
     gtime = sum(kernels[n]["avg_us"] * 1e-6 * kernels[n]["launches"] / args.steps
                 for n in gemm_names if n in kernels)
     disp = kernels.get("dispatch_scatter", {})
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FWD if fwd_only else METRIC,
         "value": S_in * args.steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -276,9 +282,13 @@ def main():
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg["workload"], "tokens": S_in, "moe_tokens": moe.S, "H": wl.H,
                    "H_ffn": wl.Hf, "experts": wl.E, "top_k": wl.K, "router_bias_beta": wl.beta,
-                   "maxvio_measured": maxvio, "parallelism": "single GPU, all experts resident"},
+                   "maxvio_measured": maxvio, "parallelism": "single GPU, all experts resident",
+                   "step": "forward" if fwd_only else "forward+backward"},
         "roofline": roof,
         "grouped_gemm_mfma_frac": (gflops / gtime) / PEAK_BF16 if gtime > 0 else None,
+        "grouped_gemm_hbm_frac": (
+            sum(kernel_model(n, mcfg, counts)[1] for n in gemm_names if n in kernels) / gtime
+            / PEAK_HBM if gtime > 0 else None),
         "dispatch_hbm_frac": disp.get("frac") if disp.get("bound") == "hbm" else None,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "kernels_frac": {k: round(v["frac"], 4) for k, v in kernels.items() if "frac" in v},
@@ -292,10 +302,11 @@ def main():
     if not args.no_cpu_baseline:
         del x, Wg, dout, W1, W3, W2, layer, moe
         torch.cuda.empty_cache()
-        default_sample = {"c1": 64, "c2": 4096, "c3": 1024, "c4": 16, "c5": 512}[args.config]
+        default_sample = {"c1": 64, "c2": 4096, "c3": 1024, "c4": 16, "c5": 512,
+                          "c6": 8}[args.config]
         say(f"GPU part done ({ms_per_step:.2f} ms/step); timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.config, args.maxvio,
-                                           args.cpu_sample or default_sample)
+                                           args.cpu_sample or default_sample, fwd_only)
     print(json.dumps(out), flush=True)
     if args.kernels:
         for k, v in kernels.items():

@@ -62,7 +62,10 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   const int64_t R = S * K;
   L.nb = (int)((S + 255) / 256);
   L.epad = (E + 15) / 16 * 16;
-  L.max_tiles = (int)((R + (int64_t)E * (kGemmBM - 1)) / kGemmBM);
+  // few rows per expert (small batches: the grouped GEMMs stream weights)
+  // take 64-row M tiles, so that a tile is not mostly padding
+  L.bm = (dtype == MOE_BF16 && R <= (int64_t)kFewRows * E) ? kGemmBMFew : kGemmBM;
+  L.max_tiles = (int)((R + (int64_t)E * (L.bm - 1)) / L.bm);
   // dWg row items: about 2048 (item, 2048-column chunk) blocks whatever the skew
   const int hblocks = (H + 2047) / 2048;
   int rb = 16;

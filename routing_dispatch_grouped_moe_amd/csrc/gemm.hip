@@ -385,13 +385,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int MI = WM / 32, NJ = WN / 32;    // 32x32 MFMA blocks per wavefront
   constexpr int kTileA = BM * kBK * 2, kTileB = BN * kBK * 2;
   constexpr int kStage = kTileA + NB * kTileB;
-  // This form serves the fp32 weight gradients only.  The overwriting kind
-  // takes the transposed MFMA result (four consecutive columns per lane),
-  // staged through LDS and stored as whole rows; the accumulating kind keeps
-  // the direct result (each 4-byte load/store instruction covers two whole
-  // 128-byte rows of the gradient it adds to).
-  static_assert(epi_f32(EPI), "the eight-wavefront form computes fp32 weight gradients");
-  constexpr bool kSwapAB = EPI != EPI_F32_ACC;
+  // This form serves the fp32 weight gradients and, with 64-row M tiles,
+  // the M-grouped products of few-row experts.  The overwriting weight
+  // gradient takes the transposed MFMA result (four consecutive columns per
+  // lane), staged through LDS and stored as whole rows; the others keep the
+  // direct result (each 4-byte load/store instruction of the accumulating
+  // kind covers two whole 128-byte rows of the gradient it adds to; the
+  // few-row outputs are small).
+  static_assert(epi_f32(EPI) || (!KGROUP && BM == kGemmBMFew),
+                "the eight-wavefront form: fp32 weight gradients, few-row M-grouped products");
+  constexpr bool kSwapAB = EPI == EPI_F32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int e, valid, m0, n0;
@@ -1282,23 +1285,24 @@ __device__ int block_exclusive_scan_1024_g(int v, int* sh, int* total) {
 }
 
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ cu, int E,
-                                                          int max_tiles, int2* __restrict__ tiles,
+                                                          int bm, int max_tiles,
+                                                          int2* __restrict__ tiles,
                                                           int32_t* __restrict__ ntiles) {
   __shared__ int sh[1024];
   const int e = threadIdx.x;
   // A malformed cu (not monotone) yields no tiles for that expert rather than
   // a table overflow.
   const int c = e < E ? max(0, cu[e + 1] - cu[e]) : 0;
-  const int nt = (c + kGemmBM - 1) / kGemmBM;
+  const int nt = (c + bm - 1) / bm;
   int total;
   const int start = block_exclusive_scan_1024_g(nt, sh, &total);
-  for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * kGemmBM);
+  for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
   if (e == 0) *ntiles = min(total, max_tiles);
 }
 
 void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hipStream_t s) {
   TimedLaunch tl("gemm_tile_table", s);
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, cu, E, L.max_tiles,
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, cu, E, L.bm, L.max_tiles,
                      reinterpret_cast<int2*>(ws + L.tiles), reinterpret_cast<int32_t*>(ws + L.ntiles));
 }
 
@@ -1306,7 +1310,8 @@ void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hi
 template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI,
           bool W4 = true>
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
-  static_assert(KGROUP || BM == kGemmBM, "M-grouped tiles follow the tile table");
+  static_assert(KGROUP || BM == kGemmBM || (BM == kGemmBMFew && !W4),
+                "M-grouped tiles follow the tile table");
   const int bm = bf16 ? BM : kBMf, bn = bf16 ? BN : kBNf;
   p.ntn = (p.N + bn - 1) / bn;
   int blocks;
@@ -1401,8 +1406,12 @@ void launch_ffn_up(const void* xd, const int32_t* cu, const void* W1, const void
   p.A0 = xd; p.lda = H;
   p.B0 = W1; p.B1 = W3; p.ldb = Hf; p.sBe = (int64_t)H * Hf;
   p.C0 = h1; p.C1 = h3; p.C2 = a; p.ldc = Hf;
-  gemm_launch<256, 128, true, false, true, false, false, EPI_SWIGLU_FWD>("ffn_up", p, L.max_tiles,
-                                                                         bf16, s);
+  if (L.bm == kGemmBMFew)
+    gemm_launch<kGemmBMFew, 128, true, false, true, false, false, EPI_SWIGLU_FWD, false>(
+        "ffn_up", p, L.max_tiles, bf16, s);
+  else
+    gemm_launch<256, 128, true, false, true, false, false, EPI_SWIGLU_FWD>("ffn_up", p,
+                                                                           L.max_tiles, bf16, s);
 }
 
 void launch_ffn_down(const void* a, const int32_t* cu, const void* W2, void* y, int64_t R, int H,
@@ -1415,8 +1424,12 @@ void launch_ffn_down(const void* a, const int32_t* cu, const void* W2, void* y, 
   p.B0 = W2; p.ldb = H; p.sBe = (int64_t)Hf * H;
   p.C0 = y; p.ldc = H;
   split_args(p, L, ws);
-  gemm_launch<256, 256, true, false, false, false, false, EPI_STORE>("ffn_down", p, L.max_tiles,
-                                                                     bf16, s);
+  if (L.bm == kGemmBMFew)
+    gemm_launch<kGemmBMFew, 256, true, false, false, false, false, EPI_STORE, false>(
+        "ffn_down", p, L.max_tiles, bf16, s);
+  else
+    gemm_launch<256, 256, true, false, false, false, false, EPI_STORE>("ffn_down", p, L.max_tiles,
+                                                                       bf16, s);
 }
 
 void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void* h1,
@@ -1430,8 +1443,12 @@ void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void
   p.B0 = W2; p.ldb = H; p.sBe = (int64_t)Hf * H;
   p.C0 = dh1; p.C1 = dh3; p.ldc = Hf;
   p.X0 = h1; p.X1 = h3;
-  gemm_launch<256, 256, true, true, false, false, false, EPI_SWIGLU_BWD>("bwd_dA", p, L.max_tiles,
-                                                                         bf16, s);
+  if (L.bm == kGemmBMFew)
+    gemm_launch<kGemmBMFew, 256, true, true, false, false, false, EPI_SWIGLU_BWD, false>(
+        "bwd_dA", p, L.max_tiles, bf16, s);
+  else
+    gemm_launch<256, 256, true, true, false, false, false, EPI_SWIGLU_BWD>("bwd_dA", p,
+                                                                           L.max_tiles, bf16, s);
 }
 
 void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const void* W1,
@@ -1445,8 +1462,12 @@ void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const v
   p.B0 = W1; p.B1 = W3; p.ldb = Hf; p.sBe = (int64_t)H * Hf;
   p.C0 = dxd; p.ldc = H;
   split_args(p, L, ws);
-  gemm_launch<256, 256, true, true, false, true, false, EPI_STORE>("bwd_dxd", p, L.max_tiles, bf16,
-                                                                   s);
+  if (L.bm == kGemmBMFew)
+    gemm_launch<kGemmBMFew, 256, true, true, false, true, false, EPI_STORE, false>(
+        "bwd_dxd", p, L.max_tiles, bf16, s);
+  else
+    gemm_launch<256, 256, true, true, false, true, false, EPI_STORE>("bwd_dxd", p, L.max_tiles,
+                                                                     bf16, s);
 }
 
 void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,

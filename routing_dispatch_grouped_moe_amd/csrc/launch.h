@@ -36,13 +36,16 @@ struct WsLayout {
   int nb;             // dispatch blocks of 256 tokens
   int epad;           // E rounded up to 16
   int max_tiles;      // upper bound on M tiles over all experts
+  int bm;             // rows per M tile of the grouped GEMMs (kGemmBM or kGemmBMFew)
   int dwg_rb;         // rows per dWg item (a power of two, 16..256)
   int dwg_max_items;  // upper bound on dWg items over all experts
   int tail_items;     // capacity of gemm_part in partial tiles
 };
 WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
 
-constexpr int kGemmBM = 256;  // M tile of the grouped GEMMs (rows per tile)
+constexpr int kGemmBM = 256;   // M tile of the grouped GEMMs (rows per tile)
+constexpr int kGemmBMFew = 64; // M tile when experts average at most kFewRows rows (bf16)
+constexpr int kFewRows = 32;
 
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);

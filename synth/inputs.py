@@ -47,6 +47,10 @@ CONFIGS: Dict[str, dict] = {
     "c5": dict(workload="mod50-moe-16x-top2-bf16", S=4096, B=4, T=2048, C=1024, H=4096,
                Hf=5632, E=16, K=2, dtype="bf16", seed=4, x_std=1.0, w_std=0.02,
                bias="none"),
+    # inference (decode) shape of the MoonEP layer: 128 tokens, about 2.7 rows
+    # per expert, forward only; the grouped GEMMs stream the expert weights
+    "c6": dict(workload="moonep-384x-top8-decode128-bf16", S=128, H=7168, Hf=2048, E=384, K=8,
+               dtype="bf16", seed=5, x_std=1.0, w_std=0.02, bias="none", forward_only=True),
 }
 
 

@@ -74,6 +74,7 @@ FULL = [
     ("c3_zipf_full", "c3", None),
     ("c4_moonep_full_maxvio0.2", "c4", 0.2),
     ("c4_moonep_full_maxvio20", "c4", 20.0),
+    ("c6_decode_full", "c6", None),
 ]
 
 

@@ -100,6 +100,13 @@ CASES = [
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
+    # decode shape: about one row per expert, many experts empty; the
+    # M-grouped products take 64-row tiles (at most 32 rows per expert on
+    # average), forward and backward
+    ("c6_decode_small", "c6", dict(S=48, H=512, Hf=256)),
+    # 64-row tiles with a hot expert spanning several of them (ragged tail):
+    # 400 rows over 16 experts, the Zipf-biased top expert takes most tokens
+    ("c4_few_rows_hot_expert", "c4", dict(S=200, H=256, Hf=384, E=16, K=2, beta=4.0)),
 ]
 
 
