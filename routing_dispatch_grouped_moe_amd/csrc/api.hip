@@ -89,6 +89,11 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   // per tile the problem can have
   L.tail_items = (int)std::min<int64_t>(256, (int64_t)8 * L.max_tiles * ((H + 255) / 256));
   L.gemm_part = off; off = align256(off + (size_t)std::max(L.tail_items, 1) * 256 * 256 * 4);
+  L.route_groups = (int)((S + 31) / 32);
+  L.route_parts = dtype == MOE_BF16 ? route_parts(S, H, L.epad) : 1;
+  L.route_part = off;
+  off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
+  L.route_tickets = off; off = align256(off + (size_t)std::max(L.route_groups, 1) * 4);
   L.total = off;
   return L;
 }
@@ -190,10 +195,12 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;
   launch_fill_i32(counts, 0, d->E, s);
-  launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, s);
+  int32_t* tickets = reinterpret_cast<int32_t*>(w + L.route_tickets);
+  launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, tickets, L.route_groups, s);
   launch_route(x, w + L.wgT, bias, logits, topk_idx, gates, counts,
                reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, L.epad, d->K,
-               (d->flags & MOE_F_RENORM) != 0, bf16, s);
+               (d->flags & MOE_F_RENORM) != 0, bf16, L.route_parts,
+               reinterpret_cast<float*>(w + L.route_part), tickets, s);
   return launched();
 }
 
@@ -321,7 +328,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
     launch_bwd_dxd(b->dh1, b->dh3, sv->cu_seqlens, sv->W1, sv->W3, b->dxd, R, H, Hf, E, L, w, bf16,
                    s);
   launch_bwd_dw13(sv->xd, b->dh1, b->dh3, sv->cu_seqlens, dW1, dW3, R, H, Hf, E, accum, bf16, s);
-  launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, s);
+  launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, nullptr, 0, s);
   launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16, s);
   launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
   return launched();

@@ -32,6 +32,8 @@ struct WsLayout {
   size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
   size_t dwg_part;    // [dwg_max_items, H] fp32 partial router-weight gradient per item
   size_t gemm_part;   // [tail_items, 256 * 256] fp32 K-split partial tiles of the last GEMM wave
+  size_t route_part;  // [groups, route_parts, 32, epad] fp32 partial logits of a split router
+  size_t route_tickets; // [groups] int32 parts finished per 32-token group
   size_t total;
   int nb;             // dispatch blocks of 256 tokens
   int epad;           // E rounded up to 16
@@ -40,6 +42,8 @@ struct WsLayout {
   int dwg_rb;         // rows per dWg item (a power of two, 16..256)
   int dwg_max_items;  // upper bound on dWg items over all experts
   int tail_items;     // capacity of gemm_part in partial tiles
+  int route_groups;   // 32-token groups of the router
+  int route_parts;    // K parts per group (1: no split)
 };
 WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
 
@@ -49,10 +53,14 @@ constexpr int kFewRows = 32;
 
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
-void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16, hipStream_t s);
+void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16,
+                         int32_t* tickets, int ntickets, hipStream_t s);
+// K parts per 32-token group of the bf16 router (1: no split)
+int route_parts(int64_t S, int H, int epad);
 void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,
                   float* gates, int32_t* counts, uint32_t* status, int64_t S, int H, int E, int epad,
-                  int K, bool renorm, bool bf16, hipStream_t s);
+                  int K, bool renorm, bool bf16, int nparts, float* rpart, int32_t* tickets,
+                  hipStream_t s);
 
 void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
                      int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,

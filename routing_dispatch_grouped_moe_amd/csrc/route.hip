@@ -16,7 +16,10 @@
 // wavefront on all eight: each lane holds
 // E/64 64-bit order keys (ordered logit bits : ~expert), and K rounds of a
 // butterfly max pick the winners.  Counts come from an LDS histogram flushed
-// with one atomic per (block, expert).
+// with one atomic per (block, expert).  With few token blocks (small
+// batches) the H reduction is split over several blocks per 32 tokens: each
+// writes its fp32 partial logits, and the block that finishes last (a
+// per-group ticket) sums the parts in part order and runs the top-K.
 #include <algorithm>
 
 #include "dev_common.h"
@@ -27,6 +30,7 @@ namespace moe {
 
 constexpr int kRouteBT = 32;
 constexpr int kRouteWaves = 8;  // bf16 router: 4 load wavefronts + 4 MFMA wavefronts
+constexpr int kRouteMaxParts = 16;  // K parts per token group of the split router
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -55,7 +59,11 @@ void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 // WgT[e][h] = Wg[h][e] for e < E, zero rows for E <= e < epad.
 template <bool BF16>
 __global__ __launch_bounds__(256) void transpose_wg_kernel(const void* Wg, void* wgT, int H, int E,
-                                                           int epad) {
+                                                           int epad, int32_t* tickets,
+                                                           int ntickets) {
+  // the router's per-group tickets start every call at zero
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < ntickets; i += 256) tickets[i] = 0;
   __shared__ float tile[32][33];
   const int h0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -71,13 +79,15 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const void* Wg, void*
 }
 
 void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16,
-                         hipStream_t s) {
+                         int32_t* tickets, int ntickets, hipStream_t s) {
   dim3 grid((H + 31) / 32, (epad + 31) / 32);
   TimedLaunch tl("route_wg_transpose", s);
   if (bf16)
-    hipLaunchKernelGGL(transpose_wg_kernel<true>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad);
+    hipLaunchKernelGGL(transpose_wg_kernel<true>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad,
+                       tickets, ntickets);
   else
-    hipLaunchKernelGGL(transpose_wg_kernel<false>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad);
+    hipLaunchKernelGGL(transpose_wg_kernel<false>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad,
+                       tickets, ntickets);
 }
 
 // ------------------------------------------------------------ router GEMM --
@@ -213,19 +223,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
                                                          int32_t* __restrict__ counts,
                                                          uint32_t* __restrict__ status, int S,
                                                          int H, int E, int epad, int K,
-                                                         int renorm) {
+                                                         int renorm, int nparts,
+                                                         float* __restrict__ rpart,
+                                                         int32_t* __restrict__ tickets) {
   using T = RouteTile<NCB, KS, U>;
   constexpr int NWN = 4 / KS;
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // stages, then partial logits
   __shared__ int hist[1024];
+  __shared__ int last_part;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // wavefronts 0-3 compute, 4-7 load on behalf of compute wavefront w
   const bool loader = wv >= 4;
   const int w = wv & 3;
   const int wn = w % NWN, ksi = w / NWN;
-  const int t0 = blockIdx.x * kRouteBT;
+  // token group g, K part `part` of nparts (steps [s_lo, s_lo + nsteps))
+  const int g = blockIdx.x / nparts, part_id = blockIdx.x - g * nparts;
+  const int t0 = g * kRouteBT;
   const int nt = min(kRouteBT, S - t0);
+  const int ns_all = H / T::BK;
+  const int s_lo = part_id * ns_all / nparts;
+  const int nsteps = (part_id + 1) * ns_all / nparts - s_lo;
   for (int e = tid; e < E; e += 64 * kRouteWaves) hist[e] = 0;
 
   // per-lane byte offsets of this wavefront's direct loads (relative to the
@@ -252,7 +270,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
   // loads of K slice kt into stage st (past the end of K they read zeros or
   // rows of this block's own range, into a stage that is not read again)
   auto issue = [&](int kt, int st) {
-    const uint32_t k2 = (uint32_t)kt * T::BK * 2u;
+    const uint32_t k2 = (uint32_t)(s_lo + kt) * T::BK * 2u;
     const u32x4 rx = rsrc_words(xb + k2, xbytes - min(k2, xbytes));
     const u32x4 rw = rsrc_words(wb + k2, wbytes - min(k2, wbytes));
     char* sb = smem + st * T::kStage;
@@ -265,7 +283,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
   f32x4 acc[2][NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[0][cb] = acc[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nsteps = H / T::BK;
   if (loader) {
 #pragma unroll
     for (int st = 0; st < T::NS - 1; ++st) issue(st, st);
@@ -312,6 +329,54 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
   // 16x16 MFMA result: lane holds column (lane % 16), rows 4 (lane / 16) + i;
   // slice 0 carries the bias
   float* part = reinterpret_cast<float*>(smem);
+  if constexpr (KS == 1) {
+    if (nparts > 1) {
+      // this part's logits (no bias) -> rpart[group][part][32][epad]
+      float* gp = rpart + (size_t)blockIdx.x * kRouteBT * epad;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int nbk = wn + cb * NWN;
+        if (!loader && nbk * 16 < epad) {
+          const int col = nbk * 16 + r16;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gp[(size_t)(rb * 16 + q * 4 + i) * epad + col] = acc[rb][cb][i];
+        }
+      }
+      // publish the part; the group's last block to take a ticket sums them
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) last_part = atomicAdd(&tickets[g], 1) == nparts - 1;
+      __syncthreads();
+      if (!last_part) return;
+      __threadfence();
+      // sum the parts in part order, four logits a lane, all parts' loads
+      // in flight together (epad is a multiple of 16, so a 4-float piece
+      // never crosses a row)
+      const f32x4* g0 = reinterpret_cast<const f32x4*>(rpart + (size_t)g * nparts * kRouteBT * epad);
+      const int n4 = kRouteBT * epad / 4, pstride = kRouteBT * epad / 4;
+      for (int i = tid; i < n4; i += 64 * kRouteWaves) {
+        f32x4 pv[kRouteMaxParts];
+#pragma unroll
+        for (int pp = 0; pp < kRouteMaxParts; ++pp)
+          if (pp < nparts) pv[pp] = g0[(size_t)pp * pstride + i];
+        f32x4 v = pv[0];
+#pragma unroll
+        for (int pp = 1; pp < kRouteMaxParts; ++pp)
+          if (pp < nparts) v += pv[pp];
+        const int col = (4 * i) % epad;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (bias != nullptr && col + c < E) v[c] += bias[col + c];
+        reinterpret_cast<f32x4*>(part)[i] = v;
+      }
+      __syncthreads();
+      route_tail<NCB, kRouteWaves>(part, hist, 1, logits, idx, gates, counts, status, t0, nt, E,
+                                   epad, K, renorm);
+      return;
+    }
+  }
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int nbk = wn + cb * NWN;
@@ -364,7 +429,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 template <int NCB, int KS, int U>
 static void route_launch_t(const void* x, const void* wgT, const float* bias, float* logits,
                            int32_t* idx, float* gates, int32_t* counts, uint32_t* status, int64_t S,
-                           int H, int E, int epad, int K, bool renorm, hipStream_t s) {
+                           int H, int E, int epad, int K, bool renorm, int nparts, float* rpart,
+                           int32_t* tickets, hipStream_t s) {
   using T = RouteTile<NCB, KS, U>;
   const size_t lds = std::max((size_t)T::NS * T::kStage, (size_t)KS * kRouteBT * epad * sizeof(float));
   auto kern = route_mfma_kernel<NCB, KS, U>;
@@ -373,15 +439,29 @@ static void route_launch_t(const void* x, const void* wgT, const float* bias, fl
   if (!attr)
     attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
-  const int blocks = (int)((S + kRouteBT - 1) / kRouteBT);
+  const int blocks = (int)((S + kRouteBT - 1) / kRouteBT) * nparts;
   TimedLaunch tl("route", s);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kRouteWaves), lds, s, x, wgT, bias, logits, idx, gates,
-                     counts, status, (int)S, H, E, epad, K, renorm ? 1 : 0);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kRouteWaves), lds, s, x, wgT, bias, logits, idx,
+                     gates, counts, status, (int)S, H, E, epad, K, renorm ? 1 : 0, nparts, rpart,
+                     tickets);
+}
+
+// Up to kRouteMaxParts parts while the grid stays within two blocks per compute unit
+// and every part keeps at least four K steps.
+int route_parts(int64_t S, int H, int epad) {
+  const RouteSplit sp = route_split(epad);
+  if (sp.ks != 1) return 1;
+  const int64_t groups = (S + kRouteBT - 1) / kRouteBT;
+  const int steps = H / (32 * sp.u);
+  int P = 1;
+  while (P < kRouteMaxParts && groups * P * 2 <= 512 && steps >= 4 * P * 2) P *= 2;
+  return P;
 }
 
 void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,
                   float* gates, int32_t* counts, uint32_t* status, int64_t S, int H, int E,
-                  int epad, int K, bool renorm, bool bf16, hipStream_t s) {
+                  int epad, int K, bool renorm, bool bf16, int nparts, float* rpart,
+                  int32_t* tickets, hipStream_t s) {
   if (S <= 0) return;
   if (!bf16) {
     const size_t lds = (size_t)kRouteBT * epad * sizeof(float);
@@ -400,7 +480,7 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
 #define ROUTE_CASE(N, KS_, U_)                                                                  \
   if (sp.ks == KS_ && sp.u == U_ && sp.ncb <= N) {                                             \
     route_launch_t<N, KS_, U_>(x, wgT, bias, logits, idx, gates, counts, status, S, H, E, epad, \
-                               K, renorm, s);                                                  \
+                               K, renorm, nparts, rpart, tickets, s);                          \
     return;                                                                                    \
   }
   ROUTE_CASE(1, 4, 1) ROUTE_CASE(1, 2, 1) ROUTE_CASE(2, 2, 1) ROUTE_CASE(1, 1, 2)
