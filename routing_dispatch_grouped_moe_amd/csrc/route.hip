@@ -17,9 +17,10 @@
 // E/64 64-bit order keys (ordered logit bits : ~expert), and K rounds of a
 // butterfly max pick the winners.  Counts come from an LDS histogram flushed
 // with one atomic per (block, expert).  With few token blocks (small
-// batches) the H reduction is split over several blocks per 32 tokens: each
-// writes its fp32 partial logits, and the block that finishes last (a
-// per-group ticket) sums the parts in part order and runs the top-K.
+// batches, up to 1024 tokens) the H reduction is split over several blocks
+// per 32 tokens: each writes its fp32 partial logits, and the block that
+// finishes last (a per-group ticket) sums the parts in part order and runs
+// the top-K.
 #include <algorithm>
 
 #include "dev_common.h"
@@ -446,15 +447,22 @@ static void route_launch_t(const void* x, const void* wgT, const float* bias, fl
                      tickets);
 }
 
-// Up to kRouteMaxParts parts while the grid stays within two blocks per compute unit
-// and every part keeps at least four K steps.
+// Up to kRouteMaxParts parts while the grid stays within a quarter of the
+// compute units and every part keeps at least four K steps.  The split costs
+// each part an agent-scope release and the last one an acquire, which on
+// gfx950 write back and invalidate the L2 of its XCD; every other block of
+// that XCD then fetches its router-weight slices again.  That is cheap next
+// to the work of a few groups but not once the groups alone fill the chip:
+// measured at 8192 tokens (256 groups), two parts took the router from 146
+// to 359 us at 384 experts and from 26 to 210 us at 64 experts, while at 128
+// tokens (4 groups, 384 experts) four parts took it from 130 to 60 us.
 int route_parts(int64_t S, int H, int epad) {
   const RouteSplit sp = route_split(epad);
   if (sp.ks != 1) return 1;
   const int64_t groups = (S + kRouteBT - 1) / kRouteBT;
   const int steps = H / (32 * sp.u);
   int P = 1;
-  while (P < kRouteMaxParts && groups * P * 2 <= 512 && steps >= 4 * P * 2) P *= 2;
+  while (P < kRouteMaxParts && groups * P * 2 <= 64 && steps >= 4 * P * 2) P *= 2;
   return P;
 }
 
