@@ -10,9 +10,13 @@
 // dx           dx[s] = sum_k dxd[row] + sum_k dl[s,idx_k] Wg[:, idx_k]
 // dwg          dWg[:, e] = sum over expert e's rows of dl_row[r] * xd[r]
 //
-// gfx950 design: one wavefront per token; each lane streams 16-byte pieces
-// (8 bf16) of the token's rows, accumulates in fp32 and writes 16-byte
-// pieces, so every row read and write is a full coalesced 1-KB wave access.
+// gfx950 design: each lane streams 16-byte pieces (8 bf16) of a token's
+// rows, accumulates in fp32 and writes 16-byte pieces, so every row read and
+// write is a full coalesced 1-KB wave access.  combine and dx give each
+// wavefront one 128-piece column chunk of one token (a 7168-wide row is
+// seven wavefronts, so the launch ends evenly across the compute units);
+// combine_bwd keeps one wavefront per token because its gate gradient
+// reduces over the whole row.
 // The router-weight gradient reduces over each expert's contiguous rows in
 // row order (deterministic), cut into row items of bounded size so a hot
 // expert spreads over many blocks; a second kernel adds the items in order.
@@ -63,6 +67,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
 }
 
 constexpr int kCombU = 2;  // column chunks (of 64 pieces) per iteration
+// combine and dx: one wavefront per (token, chunk of kCombChunk pieces), so
+// a wide row spreads over several wavefronts and the last wave of a launch
+// is short
+constexpr int kCombChunk = 64 * kCombU;
 
 template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
@@ -72,8 +80,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int64_t R) {
   using PC = Piece<BF16>;
   const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (s >= S) return;
+  const int pieces = H / PC::kEl;
+  const int nch = (pieces + kCombChunk - 1) / kCombChunk;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)S * nch) return;
+  const int s = (int)(item / nch);
   int rk = -1;
   float gk = 0.f;
   if (lane < K) {
@@ -89,8 +100,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     g[k] = k < K ? __shfl(gk, k, kWave) : 0.f;
     rs[k] = row_rsrc<BF16>(y, r, H, k < K && r >= 0);
   }
-  const int pieces = H / PC::kEl;
-  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
+  {
+    const int p0 = (int)(item - (int64_t)s * nch) * kCombChunk + lane;
     u32x4 w[kCombU][KT];
 #pragma unroll
     for (int u = 0; u < kCombU; ++u)
@@ -128,8 +139,9 @@ template <bool BF16, int KT>
 struct CombineLaunch {
   static void run(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
                   int H, int K, int64_t R, hipStream_t s) {
-    hipLaunchKernelGGL((combine_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0, s,
-                       y, row_of, gates, out, (int)S, H, K, R);
+    const int64_t items = S * ((H / Piece<BF16>::kEl + kCombChunk - 1) / kCombChunk);
+    hipLaunchKernelGGL((combine_kernel<BF16, KT>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0,
+                       s, y, row_of, gates, out, (int)S, H, K, R);
   }
 };
 
@@ -267,8 +279,11 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dxd,
                                                  int64_t R) {
   using PC = Piece<BF16>;
   const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (s >= S) return;
+  const int pieces = H / PC::kEl;
+  const int nch = (pieces + kCombChunk - 1) / kCombChunk;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)S * nch) return;
+  const int s = (int)(item / nch);
   int rk = -1, ek = -1;
   float dk = 0.f;
   if (lane < K) {
@@ -288,8 +303,8 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dxd,
     rr[k] = row_rsrc<BF16>(dxd, r, H, r >= 0);
     re[k] = row_rsrc<BF16>(wgT, ex, H, ex >= 0);
   }
-  const int pieces = H / PC::kEl;
-  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
+  {
+    const int p0 = (int)(item - (int64_t)s * nch) * kCombChunk + lane;
     u32x4 wr[kCombU][KT], we[kCombU][KT];
 #pragma unroll
     for (int u = 0; u < kCombU; ++u)
@@ -328,8 +343,9 @@ struct DxLaunch {
   static void run(const void* dxd, const int32_t* row_of, const int32_t* idx, const float* dlogits,
                   const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R,
                   hipStream_t s) {
-    hipLaunchKernelGGL((dx_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0, s, dxd,
-                       row_of, idx, dlogits, wgT, dx, (int)S, H, E, K, R);
+    const int64_t items = S * ((H / Piece<BF16>::kEl + kCombChunk - 1) / kCombChunk);
+    hipLaunchKernelGGL((dx_kernel<BF16, KT>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s,
+                       dxd, row_of, idx, dlogits, wgT, dx, (int)S, H, E, K, R);
   }
 };
 
