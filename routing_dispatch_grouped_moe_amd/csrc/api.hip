@@ -196,7 +196,8 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   const bool bf16 = d->dtype == MOE_BF16;
   launch_fill_i32(counts, 0, d->E, s);
   int32_t* tickets = reinterpret_cast<int32_t*>(w + L.route_tickets);
-  launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, tickets, L.route_groups, s);
+  launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, bf16, tickets, L.route_groups,
+                      s);
   launch_route(x, w + L.wgT, bias, logits, topk_idx, gates, counts,
                reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, L.epad, d->K,
                (d->flags & MOE_F_RENORM) != 0, bf16, L.route_parts,
@@ -328,7 +329,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
     launch_bwd_dxd(b->dh1, b->dh3, sv->cu_seqlens, sv->W1, sv->W3, b->dxd, R, H, Hf, E, L, w, bf16,
                    s);
   launch_bwd_dw13(sv->xd, b->dh1, b->dh3, sv->cu_seqlens, dW1, dW3, R, H, Hf, E, accum, bf16, s);
-  launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, nullptr, 0, s);
+  launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, false, nullptr, 0, s);
   launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16, s);
   launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
   return launched();

@@ -53,8 +53,9 @@ constexpr int kFewRows = 32;
 
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// blocked: the bf16 router's K-blocked layout [H / 32][epad][32]; else [epad][H]
 void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16,
-                         int32_t* tickets, int ntickets, hipStream_t s);
+                         bool blocked, int32_t* tickets, int ntickets, hipStream_t s);
 // K parts per 32-token group of the bf16 router (1: no split)
 int route_parts(int64_t S, int H, int epad);
 void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,

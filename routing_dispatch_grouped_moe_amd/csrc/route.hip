@@ -5,10 +5,12 @@
 // routing sparse).
 //
 // gfx950 design: a block owns 32 tokens.  The router GEMM runs on MFMA
-// (v_mfma_f32_16x16x32_bf16) against a transposed copy of the router weight,
-// WgT [Epad, H], made once per call; both operands stream through a ring of
-// LDS stages filled by direct global->LDS loads, several K slices ahead of
-// the MFMAs.  Four wavefronts issue those loads and four others read the
+// (v_mfma_f32_16x16x32_bf16) against a transposed copy of the router weight
+// made once per call, K-blocked as [H / 32][Epad][32] so that each direct
+// load of 16 experts' K32 slices is 1 KB of whole cache lines (a row-major
+// [Epad][H] copy would give 64 bytes of each of 16 lines); both operands
+// stream through a ring of LDS stages filled by direct global->LDS loads,
+// several K slices ahead of the MFMAs.  Four wavefronts issue those loads and four others read the
 // stages and run the MFMAs, so a stall of the address unit never holds up
 // the matrix core.  The MFMA wavefronts split the 16-expert column blocks,
 // or the H reduction when there are fewer than four column blocks (partial
@@ -57,8 +59,13 @@ void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
 }
 
-// WgT[e][h] = Wg[h][e] for e < E, zero rows for E <= e < epad.
-template <bool BF16>
+// WgT[e][h] = Wg[h][e] for e < E, zero rows for E <= e < epad.  Row-major
+// [epad][H] (one contiguous row per expert, for the fp32 router and the
+// dispatch backward), or K-blocked [H / 32][epad][32] for the bf16 router:
+// there one K32 slice of every expert row is 64 contiguous bytes and the
+// slices of consecutive experts are adjacent, so a direct load of 16
+// experts' slices reads 1 KB of whole cache lines.
+template <bool BF16, bool BLOCKED>
 __global__ __launch_bounds__(256) void transpose_wg_kernel(const void* Wg, void* wgT, int H, int E,
                                                            int epad, int32_t* tickets,
                                                            int ntickets) {
@@ -75,20 +82,26 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const void* Wg, void*
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
     const int e = e0 + i, h = h0 + tx;
-    if (e < epad && h < H) store1<BF16>(wgT, (int64_t)e * H + h, tile[tx][i]);
+    if (e < epad && h < H) {
+      const int64_t o = BLOCKED ? ((int64_t)(h >> 5) * epad + e) * 32 + (h & 31) : (int64_t)e * H + h;
+      store1<BF16>(wgT, o, tile[tx][i]);
+    }
   }
 }
 
 void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool bf16,
-                         int32_t* tickets, int ntickets, hipStream_t s) {
+                         bool blocked, int32_t* tickets, int ntickets, hipStream_t s) {
   dim3 grid((H + 31) / 32, (epad + 31) / 32);
   TimedLaunch tl("route_wg_transpose", s);
-  if (bf16)
-    hipLaunchKernelGGL(transpose_wg_kernel<true>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad,
-                       tickets, ntickets);
+  if (bf16 && blocked)
+    hipLaunchKernelGGL((transpose_wg_kernel<true, true>), grid, dim3(256), 0, s, Wg, wgT, H, E,
+                       epad, tickets, ntickets);
+  else if (bf16)
+    hipLaunchKernelGGL((transpose_wg_kernel<true, false>), grid, dim3(256), 0, s, Wg, wgT, H, E,
+                       epad, tickets, ntickets);
   else
-    hipLaunchKernelGGL(transpose_wg_kernel<false>, grid, dim3(256), 0, s, Wg, wgT, H, E, epad,
-                       tickets, ntickets);
+    hipLaunchKernelGGL((transpose_wg_kernel<false, false>), grid, dim3(256), 0, s, Wg, wgT, H, E,
+                       epad, tickets, ntickets);
 }
 
 // ------------------------------------------------------------ router GEMM --
@@ -211,7 +224,7 @@ __device__ __forceinline__ void route_tail(float* part, int* hist, int ks, float
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
-// bf16 router: x [S, H] times the transposed weight WgT [epad, H] on
+// bf16 router: x [S, H] times the K-blocked transposed weight on
 // v_mfma_f32_16x16x32_bf16, both operands streamed through an NS-stage LDS
 // ring by direct loads; NS - 1 stages are in flight while one is computed.
 template <int NCB, int KS, int U>
@@ -263,7 +276,8 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
     for (int u = 0; u < U; ++u) {
       const int row = lane >> 2, c = (lane & 3) ^ ((row >> 2) & 3);
       const int n = (wn + cb * NWN) * 16 + row;
-      vw[cb * U + u] = ((uint32_t)n * H + ksi * 32 * U + u * 32 + c * 8) * 2u;
+      // K-blocked WgT: K32 slice ksi U + u of the stage, expert row n
+      vw[cb * U + u] = (((uint32_t)(ksi * U + u) * epad + n) * 32 + c * 8) * 2u;
     }
   const char* xb = reinterpret_cast<const char*>(x) + (int64_t)t0 * H * 2;
   const char* wb = reinterpret_cast<const char*>(wgT);
@@ -271,9 +285,10 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
   // loads of K slice kt into stage st (past the end of K they read zeros or
   // rows of this block's own range, into a stage that is not read again)
   auto issue = [&](int kt, int st) {
-    const uint32_t k2 = (uint32_t)(s_lo + kt) * T::BK * 2u;
+    const uint32_t k2 = (uint32_t)(s_lo + kt) * T::BK * 2u;                  // along a row of x
+    const uint32_t w2 = (uint32_t)(s_lo + kt) * (T::BK / 32) * epad * 64u;  // K32 blocks of WgT
     const u32x4 rx = rsrc_words(xb + k2, xbytes - min(k2, xbytes));
-    const u32x4 rw = rsrc_words(wb + k2, wbytes - min(k2, wbytes));
+    const u32x4 rw = rsrc_words(wb + w2, wbytes - min(w2, wbytes));
     char* sb = smem + st * T::kStage;
 #pragma unroll
     for (int i = 0; i < T::kXI; ++i) dma4(rx, vx[i], sb + (w * T::kXI + i) * 256);
