@@ -1,4 +1,4 @@
-"""Full-size GPU parity in the launch configuration the bench times.
+"""Full-size GPU parity in the launch configuration the bench times (the MoD block too).
 
 The layer runs exactly as in the throughput measurement (device-drawn expert
 weights, one MoELayer forward + backward at the workload's full S, H, H', E,
@@ -93,13 +93,22 @@ def test_fullsize_sampled(cid, cfg, maxvio):
     layer.backward(dout_t, x_t, Wg_t, W1, W3, W2)
     torch.cuda.synchronize()
     assert layer.status() == 0
+    check_moe_sampled(cid, layer, wl.x, x_t, wl.dout, wl.Wg, wl.bias, W1, W3, W2,
+                      np.random.default_rng(12345))
 
-    rng = np.random.default_rng(12345)
+
+def check_moe_sampled(cid, layer, x, x_t, dout, Wg, bias, W1, W3, W2, rng):
+    """Check a finished MoELayer forward + backward against the oracle (sampled as above).
+
+    x / dout: the layer's input and upstream gradient on the host (exact
+    values; dout may be float64), x_t: x on the device.  Returns the sampled
+    token indices with the oracle's out and dx on them.
+    """
+    S, H, Hf, E, K = layer.S, layer.H, layer.Hf, layer.E, layer.K
     logits = to_host(layer.logits)
     # routing: every token, bit for bit
     ts = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, size=62)]))
-    assert_close("logits[sample]", logits[ts], oracle.router_logits(wl.x[ts], wl.Wg, wl.bias),
-                 F32_TOL)
+    assert_close("logits[sample]", logits[ts], oracle.router_logits(x[ts], Wg, bias), F32_TOL)
     idx = oracle.topk_experts(logits, K)
     np.testing.assert_array_equal(to_host(layer.topk_idx), idx, err_msg="topk_idx")
     gates = oracle.gate_weights(logits, idx)
@@ -136,7 +145,7 @@ def test_fullsize_sampled(cid, cfg, maxvio):
     n = len(all_rows)
     fw = {k: np.zeros((n, Hf)) for k in ("h1", "h3", "a")}
     fw["y"] = np.zeros((n, H))
-    Xs = np.asarray(wl.x, np.float64)[tok_of[all_rows]]
+    Xs = np.asarray(x, np.float64)[tok_of[all_rows]]
     wcache = {}
     for e in np.unique(expert_of_row):
         sel = np.nonzero(expert_of_row == e)[0]
@@ -153,7 +162,7 @@ def test_fullsize_sampled(cid, cfg, maxvio):
     rloc = np.array([local[int(r)] for r in ts_rows.reshape(-1)], np.int64)
     out = oracle.combine(fw["y"], rloc, gates[toks])
     assert_close("out[tokens]", to_host(layer.out)[toks], out, BF16_TOL)
-    dy_s, dg = oracle.combine_backward(np.asarray(wl.dout)[toks], fw["y"], rloc, gates[toks])
+    dy_s, dg = oracle.combine_backward(np.asarray(dout)[toks], fw["y"], rloc, gates[toks])
     rows_t = torch.from_numpy(all_rows).cuda()
     assert_close("dy[rows]", to_host(layer.dy[rows_t]), dy_s, BF16_TOL)
     assert_close("dgates[tokens]", to_host(layer.dgates)[toks], dg, BF16_TOL)
@@ -171,7 +180,7 @@ def test_fullsize_sampled(cid, cfg, maxvio):
         bw["dxd"][sel], bw["dh1"][sel], bw["dh3"][sel] = dxd, dh1, dh3
     for name in ("dh1", "dh3", "dxd"):
         assert_close(f"{name}[rows]", to_host(getattr(layer, name)[rows_t]), bw[name], BF16_TOL)
-    dx, _ = oracle.dispatch_router_backward(bw["dxd"], rloc, dl, wl.x[toks], wl.Wg, K)
+    dx, _ = oracle.dispatch_router_backward(bw["dxd"], rloc, dl, np.asarray(x)[toks], Wg, K)
     assert_close("dx[tokens]", to_host(layer.dx)[toks], dx, BF16_TOL)
     del wcache
     _say(f"[full] {cid}: {n} rows / {len(toks)} tokens over {len(np.unique(expert_of_row))} experts ok")
@@ -182,9 +191,9 @@ def test_fullsize_sampled(cid, cfg, maxvio):
     for e in (int(order[-1]), int(nz[len(nz) // 2])):
         r0, r1 = int(cu[e]), int(cu[e + 1])
         J = np.unique(np.concatenate([[0, Hf - 1], rng.integers(0, Hf, size=6)]))
-        Xe = np.asarray(wl.x, np.float64)[tok_of[r0:r1]]
+        Xe = np.asarray(x, np.float64)[tok_of[r0:r1]]
         p = pair_of_row[r0:r1]
-        dye = gates.reshape(-1)[p][:, None] * np.asarray(wl.dout, np.float64)[p // K]
+        dye = gates.reshape(-1)[p][:, None] * np.asarray(dout, np.float64)[p // K]
         w1, w3, w2 = _host_expert(W1, e, cols=J), _host_expert(W3, e, cols=J), \
             _host_expert(W2, e, rows=J)
         cu1 = np.array([0, r1 - r0])
@@ -201,6 +210,69 @@ def test_fullsize_sampled(cid, cfg, maxvio):
             assert not bool(g[int(e)].any()), f"expert {e} has no rows but a nonzero gradient"
 
     # router weight gradient: dWg = x^T dlogits over every entry
-    want = np.asarray(wl.x, np.float64).T @ dl_gpu.astype(np.float64)
+    want = np.asarray(x, np.float64).T @ dl_gpu.astype(np.float64)
     assert_close("dWg = x^T dlogits", to_host(layer.dWg), want, F32_TOL)
     _say(f"[full] {cid}: weight gradients ok ({len(empty)} empty experts)")
+    return {"toks": toks, "out": out, "dx": dx}
+
+
+def test_mod_fullsize_sampled():
+    """The MoD+MoE block at full size (4 x 2048 tokens in, 1024 kept per sequence).
+
+    Scores over all tokens, the keep set bit for bit (the oracle selects from
+    the GPU's fp32 scores: the integer decision in the same precision), xk
+    bitwise, dm over every kept row, the inner MoE layer sampled as above on
+    x[keep] with the upstream gradient r * dout, and the merge and its
+    backward on the sampled kept tokens plus every dropped token; dw_r is
+    checked as the sum of dr x over the kept tokens (a property at any size).
+    """
+    from routing_dispatch_grouped_moe_amd import MoDMoELayer
+    _say("[full] mod: building inputs")
+    wl = make_workload("c5", host_weights=False)
+    B, T, C = wl.cfg["B"], wl.cfg["T"], wl.cfg["C"]
+    H, Hf, E, K = wl.H, wl.Hf, wl.E, wl.K
+    x_t, wr_t, Wg_t = to_dev(wl.x, "bf16"), to_dev(wl.w_r, "bf16"), to_dev(wl.Wg, "bf16")
+    dout_t = to_dev(wl.dout, "bf16")
+    W1, W3, W2 = device_expert_weights(wl.cfg, "cuda")
+    layer = MoDMoELayer(B, T, C, H, Hf, E, K, "bf16")
+    L.moe_clear_status(layer.moe.ws)
+    _say(f"[full] mod: forward + backward B={B} T={T} C={C} H={H} H'={Hf} E={E} K={K}")
+    layer.forward(x_t, wr_t, Wg_t, None, W1, W3, W2)
+    layer.backward(dout_t, x_t, wr_t, Wg_t, W1, W3, W2)
+    torch.cuda.synchronize()
+    assert layer.moe.status() == 0
+
+    x = np.asarray(wl.x)
+    dout = np.asarray(wl.dout, np.float64)
+    r_gpu = to_host(layer.r)
+    r = oracle.mod_scores(wl.x, wl.w_r).astype(np.float64)
+    assert_close("r", r_gpu, r, F32_TOL)
+    keep = oracle.mod_keep(r_gpu, B, T, C)
+    np.testing.assert_array_equal(to_host(layer.keep)[:B * C], keep, err_msg="keep_idx")
+    keep_t = torch.from_numpy(keep.astype(np.int64)).cuda()
+    assert torch.equal(layer.xk.view(torch.int16), x_t.view(torch.int16)[keep_t]), "xk"
+    dm = r[keep][:, None] * dout[keep]
+    assert_close("dm", to_host(layer.dm), dm, BF16_TOL)
+    _say("[full] mod: scores, keep set, xk and dm ok")
+
+    res = check_moe_sampled("mod", layer.moe, x[keep], layer.xk, dm, wl.Wg, None, W1, W3, W2,
+                            np.random.default_rng(777))
+    j = res["toks"]                   # sampled kept slots
+    s = keep[j]                       # their token positions
+    dropped = np.setdiff1d(np.arange(B * T), keep)
+    got_out = to_host(layer.out)
+    assert_close("out[kept sample]", got_out[s], x[s] + r[s][:, None] * res["out"], BF16_TOL)
+    np.testing.assert_array_equal(got_out[dropped], x[dropped],
+                                  err_msg="dropped tokens must pass through unchanged")
+    dr = (dout[s] * res["out"]).sum(axis=1)
+    assert_close("dr[kept sample]", to_host(layer.dr)[j], dr, BF16_TOL)
+    wr = np.asarray(wl.w_r, np.float64)
+    got_dx = to_host(layer.dx)
+    assert_close("dx[kept sample]", got_dx[s], dout[s] + res["dx"] + dr[:, None] * wr[None, :],
+                 BF16_TOL)
+    np.testing.assert_array_equal(got_dx[dropped], np.asarray(wl.dout)[dropped],
+                                  err_msg="dropped tokens: dx must equal dout")
+    dr_gpu = to_host(layer.dr)[:B * C].astype(np.float64)
+    want = (dr_gpu[:, None] * np.asarray(x[keep], np.float64)).sum(axis=0)
+    assert_close("dw_r = sum dr x", to_host(layer.dw_r), want, F32_TOL)
+    _say(f"[full] mod: merge and its backward ok ({len(j)} kept tokens sampled)")
