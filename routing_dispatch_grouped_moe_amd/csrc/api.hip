@@ -80,6 +80,7 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.base = off; off = align256(off + (size_t)L.nb * E * 4);
   L.tiles = off; off = align256(off + (size_t)std::max(L.max_tiles, 1) * 8);
   L.ntiles = off; off = align256(off + 4);
+  L.eorder = off; off = align256(off + (size_t)E * 4);
   L.dl_row = off; off = align256(off + (size_t)std::max<int64_t>(R, 1) * 4);
   L.dwg_items = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * 16);
   L.dwg_estart = off; off = align256(off + (size_t)(E + 1) * 4);
@@ -231,7 +232,7 @@ moe_status_t moe_ffn_up(const moe_dims_t* d, const void* xd, const int32_t* cu, 
   char* w = reinterpret_cast<char*>(ws);
   const int64_t R = d->S * d->K;
   if (R > 0) {
-    launch_tile_table(cu, d->E, L, w, s);
+    launch_tile_table(cu, d->E, L, w, false, s);
     launch_ffn_up(xd, cu, W1, W3, h1, h3, a, R, d->H, d->Hf, d->E, L, w, d->dtype == MOE_BF16, s);
   }
   return launched();
@@ -248,7 +249,7 @@ moe_status_t moe_ffn_down(const moe_dims_t* d, const void* a, const int32_t* cu,
   char* w = reinterpret_cast<char*>(ws);
   const int64_t R = d->S * d->K;
   if (R > 0) {
-    launch_tile_table(cu, d->E, L, w, s);
+    launch_tile_table(cu, d->E, L, w, false, s);
     launch_ffn_down(a, cu, W2, y, R, d->H, d->Hf, d->E, L, w, d->dtype == MOE_BF16, s);
   }
   return launched();
@@ -267,7 +268,7 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* d, const void* xd, const int32_t*
   const bool bf16 = d->dtype == MOE_BF16;
   const int64_t R = d->S * d->K;
   if (R > 0) {
-    launch_tile_table(cu, d->E, L, w, s);
+    launch_tile_table(cu, d->E, L, w, false, s);
     launch_ffn_up(xd, cu, W1, W3, h1, h3, a, R, d->H, d->Hf, d->E, L, w, bf16, s);
     launch_ffn_down(a, cu, W2, y, R, d->H, d->Hf, d->E, L, w, bf16, s);
   }
@@ -296,8 +297,9 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
     const WsLayout L = ws_layout(0, d->H, d->Hf, d->E, d->K, d->dtype);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = d->dtype == MOE_BF16, accum = (d->flags & MOE_F_ACCUM_GRAD) != 0;
-    launch_bwd_dw2(nullptr, nullptr, sv->cu_seqlens, dW2, 0, d->H, d->Hf, d->E, accum, bf16, s);
-    launch_bwd_dw13(nullptr, nullptr, nullptr, sv->cu_seqlens, dW1, dW3, 0, d->H, d->Hf, d->E,
+    launch_bwd_dw2(nullptr, nullptr, sv->cu_seqlens, nullptr, dW2, 0, d->H, d->Hf, d->E, accum,
+                   bf16, s);
+    launch_bwd_dw13(nullptr, nullptr, nullptr, sv->cu_seqlens, nullptr, dW1, dW3, 0, d->H, d->Hf, d->E,
                     accum, bf16, s);
     launch_dwg(nullptr, sv->cu_seqlens, nullptr, dWg, L, reinterpret_cast<char*>(ws), 0, d->H,
                d->E, accum, bf16, s);
@@ -320,15 +322,18 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
   launch_combine_bwd(dout, sv->y, sv->row_of, sv->topk_idx, sv->gates, b->dy, b->dgates, b->dlogits,
                      dl_row, d->S, H, E, K, R, bf16, s);
   if (R > 0) {
-    launch_tile_table(sv->cu_seqlens, E, L, w, s);
+    launch_tile_table(sv->cu_seqlens, E, L, w, true, s);
     launch_bwd_da(b->dy, sv->cu_seqlens, sv->W2, sv->h1, sv->h3, b->dh1, b->dh3, R, H, Hf, E, L, w,
                   bf16, s);
   }
-  launch_bwd_dw2(sv->a, b->dy, sv->cu_seqlens, dW2, R, H, Hf, E, accum, bf16, s);
+  // experts by descending row count (written by the tile table above)
+  const int32_t* eorder = R > 0 ? reinterpret_cast<const int32_t*>(w + L.eorder) : nullptr;
+  launch_bwd_dw2(sv->a, b->dy, sv->cu_seqlens, eorder, dW2, R, H, Hf, E, accum, bf16, s);
   if (R > 0)
     launch_bwd_dxd(b->dh1, b->dh3, sv->cu_seqlens, sv->W1, sv->W3, b->dxd, R, H, Hf, E, L, w, bf16,
                    s);
-  launch_bwd_dw13(sv->xd, b->dh1, b->dh3, sv->cu_seqlens, dW1, dW3, R, H, Hf, E, accum, bf16, s);
+  launch_bwd_dw13(sv->xd, b->dh1, b->dh3, sv->cu_seqlens, eorder, dW1, dW3, R, H, Hf, E, accum,
+                  bf16, s);
   launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, false, nullptr, 0, s);
   launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16, s);
   launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);

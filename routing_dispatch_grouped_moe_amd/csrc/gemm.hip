@@ -72,6 +72,7 @@ struct GemmArgs {
   const int32_t* cu;      // [E+1] row offsets of the experts
   const int2* tiles;      // M-grouped: (expert, first row inside the expert) of each M tile
   const int32_t* ntiles;  // M-grouped: number of valid M tiles
+  const int32_t* eorder;  // K-grouped: experts in dealing order (nullptr: index order)
   int E, M, N, K;         // M-grouped: N and K (K per segment); K-grouped: M and N
   int mtn, ntn;           // tiles along M (K-grouped) / along N
   const void* A0;         // row-indexed operand (second K segment in A1)
@@ -202,7 +203,8 @@ __device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2,
 }
 
 // K-grouped blocks go expert by expert (every XCD shares each expert's
-// tiles, so experts of different row counts load the XCDs evenly).  Inside
+// tiles, so experts of different row counts load the XCDs evenly), the
+// experts in the tile table's longest-first order when one is given.  Inside
 // an expert the tiles run N fastest, or with PATCH each XCD takes a
 // contiguous range walked in groups of kGroupM M tiles x all N tiles (M
 // fastest), so the tiles an XCD holds at once form a compact patch whose
@@ -215,8 +217,9 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
                                         int& valid, int& m0, int& n0) {
   if constexpr (KGROUP) {
     const int per_e = p.mtn * p.ntn;
-    e = bid / per_e;
-    const int rem = bid - e * per_e;
+    const int slot = bid / per_e;
+    const int rem = bid - slot * per_e;
+    e = p.eorder ? p.eorder[slot] : slot;
     if constexpr (PATCH) {
       const int rp = xcd_remap(rem, per_e);
       const int per_group = kGroupM * p.ntn;
@@ -1284,26 +1287,56 @@ __device__ int block_exclusive_scan_1024_g(int v, int* sh, int* total) {
   return incl - v;
 }
 
+// M tiles of every expert (M-grouped products) and, when eorder is given,
+// the order in which the K-grouped products deal out experts: by descending
+// row count, ties to the lower index.  A K-grouped tile's K loop runs over its expert's rows, so
+// under skew the hot expert's tiles are the long ones; dealt first, they
+// overlap the many short tiles instead of trailing after them.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ cu, int E,
                                                           int bm, int max_tiles,
                                                           int2* __restrict__ tiles,
-                                                          int32_t* __restrict__ ntiles) {
+                                                          int32_t* __restrict__ ntiles,
+                                                          int32_t* __restrict__ eorder) {
   __shared__ int sh[1024];
+  __shared__ __attribute__((aligned(16))) int cnt[1024];
   const int e = threadIdx.x;
   // A malformed cu (not monotone) yields no tiles for that expert rather than
   // a table overflow.
   const int c = e < E ? max(0, cu[e + 1] - cu[e]) : 0;
+  cnt[e] = e < E ? c : -1;  // past E: ranks below every expert
   const int nt = (c + bm - 1) / bm;
   int total;
-  const int start = block_exclusive_scan_1024_g(nt, sh, &total);
+  const int start = block_exclusive_scan_1024_g(nt, sh, &total);  // its barriers publish cnt
   for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
   if (e == 0) *ntiles = min(total, max_tiles);
+  if (eorder != nullptr && e < E) {
+    // rank = experts ahead of e; counts read four at a time (every thread
+    // reads the same words: broadcast), four reads in flight per iteration
+    int rank = 0;
+    const int4* c4 = reinterpret_cast<const int4*>(cnt);
+    for (int j4 = 0; j4 < (E + 15) / 16 * 4; j4 += 4) {
+      int4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = c4[j4 + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = 4 * (j4 + u);
+        rank += (v[u].x > c || (v[u].x == c && j < e)) ? 1 : 0;
+        rank += (v[u].y > c || (v[u].y == c && j + 1 < e)) ? 1 : 0;
+        rank += (v[u].z > c || (v[u].z == c && j + 2 < e)) ? 1 : 0;
+        rank += (v[u].w > c || (v[u].w == c && j + 3 < e)) ? 1 : 0;
+      }
+    }
+    eorder[rank] = e;
+  }
 }
 
-void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hipStream_t s) {
+void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, bool expert_order,
+                       hipStream_t s) {
   TimedLaunch tl("gemm_tile_table", s);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, cu, E, L.bm, L.max_tiles,
-                     reinterpret_cast<int2*>(ws + L.tiles), reinterpret_cast<int32_t*>(ws + L.ntiles));
+                     reinterpret_cast<int2*>(ws + L.tiles), reinterpret_cast<int32_t*>(ws + L.ntiles),
+                     expert_order ? reinterpret_cast<int32_t*>(ws + L.eorder) : nullptr);
 }
 
 // -------------------------------------------------------------- launches --
@@ -1470,11 +1503,12 @@ void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const v
                                                                      bf16, s);
 }
 
-void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,
-                    int Hf, int E, bool accum, bool bf16, hipStream_t s) {
+void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, const int32_t* eorder,
+                    float* dW2, int64_t R, int H, int Hf, int E, bool accum, bool bf16,
+                    hipStream_t s) {
   // dW2[e][Hf, H] = a[rows, Hf]^T * dy[rows, H]
   GemmArgs p{};
-  p.cu = cu; p.E = E; p.M = Hf; p.N = H;
+  p.cu = cu; p.eorder = eorder; p.E = E; p.M = Hf; p.N = H;
   p.A0 = a; p.lda = Hf;
   p.B0 = dy; p.ldb = H;
   p.C0 = dW2; p.ldc = H; p.sCe = (int64_t)Hf * H;
@@ -1489,11 +1523,11 @@ void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2
 }
 
 void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int32_t* cu,
-                     float* dW1, float* dW3, int64_t R, int H, int Hf, int E, bool accum,
-                     bool bf16, hipStream_t s) {
+                     const int32_t* eorder, float* dW1, float* dW3, int64_t R, int H, int Hf,
+                     int E, bool accum, bool bf16, hipStream_t s) {
   // dW1[e][H, Hf] = xd[rows, H]^T * dh1[rows, Hf]; dW3 likewise with dh3.
   GemmArgs p{};
-  p.cu = cu; p.E = E; p.M = H; p.N = Hf;
+  p.cu = cu; p.eorder = eorder; p.E = E; p.M = H; p.N = Hf;
   p.A0 = xd; p.lda = H;
   p.B0 = dh1; p.B1 = dh3; p.ldb = Hf;
   p.C0 = dW1; p.C1 = dW3; p.ldc = Hf; p.sCe = (int64_t)H * Hf;

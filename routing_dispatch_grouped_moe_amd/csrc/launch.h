@@ -27,6 +27,7 @@ struct WsLayout {
   size_t base;        // dispatch: [nb, E] int32 first row of each (block, expert)
   size_t tiles;       // grouped GEMM: [max_tiles] int2 (expert, first row) per M tile
   size_t ntiles;      // int32 number of valid M tiles
+  size_t eorder;      // [E] int32 experts by descending row count (ties: lower index first)
   size_t dl_row;      // [R] fp32 dlogit of each dispatched row
   size_t dwg_items;   // [dwg_max_items] int4 (expert, first row, rows, 0) row items of dWg
   size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
@@ -67,7 +68,10 @@ void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* ro
                      int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
                      int E, int K, bool bf16, hipStream_t s);
 
-void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, hipStream_t s);
+// M tiles of every expert; with expert_order also the experts by descending
+// row count into the eorder region (used by the weight-gradient products)
+void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, bool expert_order,
+                       hipStream_t s);
 
 // Grouped GEMMs (see gemm.hip for the operand layouts).
 void launch_ffn_up(const void* xd, const int32_t* cu, const void* W1, const void* W3, void* h1,
@@ -81,11 +85,14 @@ void launch_bwd_da(const void* dy, const int32_t* cu, const void* W2, const void
 void launch_bwd_dxd(const void* dh1, const void* dh3, const int32_t* cu, const void* W1,
                     const void* W3, void* dxd, int64_t R, int H, int Hf, int E, const WsLayout& L,
                     char* ws, bool bf16, hipStream_t s);
-void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, float* dW2, int64_t R, int H,
-                    int Hf, int E, bool accum, bool bf16, hipStream_t s);
+// eorder: the experts in the order their tiles are dealt (the tile table's
+// longest-first order), or nullptr for index order
+void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, const int32_t* eorder,
+                    float* dW2, int64_t R, int H, int Hf, int E, bool accum, bool bf16,
+                    hipStream_t s);
 void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int32_t* cu,
-                     float* dW1, float* dW3, int64_t R, int H, int Hf, int E, bool accum,
-                     bool bf16, hipStream_t s);
+                     const int32_t* eorder, float* dW1, float* dW3, int64_t R, int H, int Hf,
+                     int E, bool accum, bool bf16, hipStream_t s);
 
 void launch_combine(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
                     int H, int K, int64_t R, bool bf16, hipStream_t s);
