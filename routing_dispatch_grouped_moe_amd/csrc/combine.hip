@@ -15,8 +15,8 @@
 // write is a full coalesced 1-KB wave access.  combine and dx give each
 // wavefront one 128-piece column chunk of one token (a 7168-wide row is
 // seven wavefronts, so the launch ends evenly across the compute units);
-// combine_bwd keeps one wavefront per token because its gate gradient
-// reduces over the whole row.
+// combine_bwd does the same inside one block per token, whose wavefronts
+// then add up the gate gradient's partial dot products in LDS.
 // The router-weight gradient reduces over each expert's contiguous rows in
 // row order (deterministic), cut into row items of bounded size so a hot
 // expert spreads over many blocks; a second kernel adds the items in order.
@@ -153,16 +153,28 @@ void launch_combine(const void* y, const int32_t* row_of, const float* gates, vo
   else with_kt<CombineLaunch, false>(K, y, row_of, gates, out, S, H, K, R, s);
 }
 
+// combine_bwd: one block per token, one wavefront per 128-piece column chunk
+// (up to kCbWaves; wider rows give a wavefront several chunks).  Each
+// wavefront writes its chunk of dy and sums its part of every <dout, y[row]>;
+// the parts meet in LDS and wavefront 0 adds them in wavefront order, then
+// finishes the gate and logit gradients.
+constexpr int kCbWaves = 8;
+
+static int combine_bwd_waves(int H, int piece_el) {
+  const int nch = (H / piece_el + kCombChunk - 1) / kCombChunk;
+  return nch < 1 ? 1 : (nch > kCbWaves ? kCbWaves : nch);
+}
+
 template <bool BF16, int KT>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(
+__global__ __launch_bounds__(64 * kCbWaves) void combine_bwd_kernel(
     const void* __restrict__ dout, const void* __restrict__ y, const int32_t* __restrict__ row_of,
     const int32_t* __restrict__ idx, const float* __restrict__ gates, void* __restrict__ dy,
     float* __restrict__ dgates, float* __restrict__ dlogits, float* __restrict__ dl_row, int S,
     int H, int E, int K, int64_t R) {
   using PC = Piece<BF16>;
-  const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (s >= S) return;
+  __shared__ float part[kCbWaves][KT];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int s = blockIdx.x;
   int rk = -1, ek = -1;
   float gk = 0.f;
   if (lane < K) {
@@ -183,13 +195,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   }
   const __amdgpu_buffer_rsrc_t rd = row_rsrc<BF16>(dout, s, H, true);
   const int pieces = H / PC::kEl;
-  for (int p0 = lane; p0 < pieces; p0 += 64 * kCombU) {
-    u32x4 wd[kCombU], w[kCombU][KT];
+  for (int p0 = w * kCombChunk + lane; p0 < pieces; p0 += nw * kCombChunk) {
+    u32x4 wd[kCombU], wv[kCombU][KT];
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
       wd[u] = buf_load16(rd, (uint32_t)(p0 + 64 * u) * 16u);
 #pragma unroll
-      for (int k = 0; k < KT; ++k) w[u][k] = buf_load16(rs[k], (uint32_t)(p0 + 64 * u) * 16u);
+      for (int k = 0; k < KT; ++k) wv[u][k] = buf_load16(rs[k], (uint32_t)(p0 + 64 * u) * 16u);
     }
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 #pragma unroll
       for (int k = 0; k < KT; ++k) {
         float v[8], o[8];
-        PC::unpack(w[u][k], v);
+        PC::unpack(wv[u][k], v);
 #pragma unroll
         for (int i = 0; i < PC::kEl; ++i) {
           dot[k] += d[i] * v[i];
@@ -212,14 +224,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       }
     }
   }
-  float my_dg = 0.f;
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     if (k < K) {
       const float t = wave_sum(dot[k]);
-      if (lane == k) my_dg = t;
+      if (lane == 0) part[w][k] = t;
     }
   }
+  __syncthreads();
+  if (w != 0) return;
+  float my_dg = 0.f;
+  if (lane < K)
+    for (int ww = 0; ww < nw; ++ww) my_dg += part[ww][lane];
   // Renormalised softmax over the chosen experts: dl_k = g_k (dg_k - sum_j g_j dg_j).
   const float inner = wave_sum(lane < K ? gk * my_dg : 0.f);
   const float my_dl = gk * (my_dg - inner);
@@ -249,9 +265,10 @@ struct CombineBwdLaunch {
   static void run(const void* dout, const void* y, const int32_t* row_of, const int32_t* idx,
                   const float* gates, void* dy, float* dgates, float* dlogits, float* dl_row,
                   int64_t S, int H, int E, int K, int64_t R, hipStream_t s) {
-    hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT>), dim3((unsigned)((S + 3) / 4)), dim3(256), 0,
-                       s, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E,
-                       K, R);
+    const int nw = combine_bwd_waves(H, Piece<BF16>::kEl);
+    hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT>), dim3((unsigned)S), dim3(64 * nw), 0, s,
+                       dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E, K,
+                       R);
   }
 };
 
