@@ -6,7 +6,8 @@ Through the C ABI against the oracle: logits to 1e-5 normwise (both sides
 accumulate exact bf16 products in at least fp32), the top-K bit for bit
 against the oracle's selection on the GPU's own fp32 logits (the integer
 decision taken in the same precision), gates to 1e-5 and per-expert counts
-bit for bit.  S = 100 leaves a ragged last block of 4 tokens.
+bit for bit.  S = 100 leaves a ragged last block of 4 tokens.  A second test
+runs token counts on both sides of the H-split rule (split up to 1024 tokens).
 """
 import sys
 
@@ -49,6 +50,41 @@ def test_route_shapes(E, K):
     torch.cuda.synchronize()
     assert L.moe_read_status(ws) == 0
 
+    got_l = to_host(logits)
+    assert_close("logits", got_l, oracle.router_logits(wl.x, wl.Wg, wl.bias), F32_TOL)
+    want_idx = oracle.topk_experts(got_l, K)
+    np.testing.assert_array_equal(to_host(idx), want_idx, err_msg="topk_idx")
+    assert_close("gates", to_host(gates), oracle.gate_weights(got_l, want_idx), F32_TOL)
+    want_counts, _ = oracle.expert_counts(want_idx, E)
+    np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
+
+
+# (S, H, E, K): token counts around the router's H-split rule (up to 1024
+# tokens, i.e. 32 token groups, split the H reduction over 2 to 16 blocks per
+# group; more tokens do not split), at hidden sizes that allow every part count
+SPLITS = [(64, 4096, 384, 8), (500, 2048, 384, 8), (1000, 2048, 64, 4), (1024, 1024, 160, 8),
+          (1056, 1024, 160, 8)]
+
+
+@pytest.mark.parametrize("S,H,E,K", SPLITS, ids=[f"S{s}_H{h}_E{e}" for s, h, e, _ in SPLITS])
+def test_route_split_boundary(S, H, E, K):
+    print(f"[route split] S={S} H={H} E={E} K={K}", flush=True)
+    sys.stdout.flush()
+    wl = make_workload("c3", S=S, H=H, Hf=128, E=E, K=K, host_weights=False)
+    d = L.dims(S, H, wl.Hf, E, K, "bf16")
+    ws = torch.zeros(L.moe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    x, Wg = to_dev(wl.x, "bf16"), to_dev(wl.Wg, "bf16")
+    bias = torch.from_numpy(wl.bias.astype(np.float32)).cuda()
+    logits = torch.empty(S, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
+    gates = torch.empty(S, K, dtype=torch.float32, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    L.moe_clear_status(ws)
+    # twice: the per-group tickets must start from zero on every call
+    for _ in range(2):
+        L.moe_route(d, x, Wg, bias, logits, idx, gates, counts, ws)
+    torch.cuda.synchronize()
+    assert L.moe_read_status(ws) == 0
     got_l = to_host(logits)
     assert_close("logits", got_l, oracle.router_logits(wl.x, wl.Wg, wl.bias), F32_TOL)
     want_idx = oracle.topk_experts(got_l, K)
