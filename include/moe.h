@@ -203,6 +203,8 @@ typedef struct {
   const int32_t* cu_seqlens;/* [E+1] */
   const int32_t* row_of;    /* [S*K] */
   const int32_t* tok_of;    /* [S*K] */
+  const float* logits;      /* [S, E] router logits (moe_route's output); required without
+                               MOE_F_RENORM, unused with it (may be NULL) */
 } moe_saved_t;
 
 /* Intermediate gradients the backward writes (caller-owned, all required). */
@@ -213,7 +215,7 @@ typedef struct {
   void* dxd;       /* [R, H]  dtype */
   float* dgates;   /* [S, K]  <dout[s], y[row]> */
   float* dlogits;  /* [S, E]  gradient at the router logits (zero off the chosen experts
-                               under MOE_F_RENORM) */
+                               under MOE_F_RENORM, dense without it) */
 } moe_bwd_bufs_t;
 
 /*
@@ -227,8 +229,14 @@ typedef struct {
  *   dWg  [H, E] fp32 output: x^T * dlogits (the bias gets no gradient)
  *   dW1, dW3 [E, H, Hf], dW2 [E, Hf, H] fp32 outputs: experts with no rows
  *   get zeros (or are left unchanged under MOE_F_ACCUM_GRAD).
- * The selection itself has no gradient.  Requires MOE_F_RENORM (the raw
- * softmax variant is not implemented on the device: MOE_ERR_UNSUPPORTED).
+ * The selection itself has no gradient.  With MOE_F_RENORM the gates are
+ * the softmax renormalised over the K chosen experts, so dlogits is zero off
+ * them and the router terms of dx and dWg touch K experts per token.
+ * Without it (raw gates, the chosen entries of the softmax over all E
+ * experts; [FW] "What's in the box", routing/gating item read literally)
+ * dlogits[s, e] = p_e (dp_e - sum_k g_k dg_k) is dense over all experts,
+ * saved->logits is required (MOE_ERR_NULL otherwise), and dx's router term
+ * and dWg are dense products over all E.
  */
 moe_status_t moe_backward(const moe_dims_t* dims, const moe_saved_t* saved, const void* dout,
                           void* dx, float* dWg, float* dW1, float* dW3, float* dW2,

@@ -41,7 +41,7 @@ class Dims(C.Structure):
 class Saved(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "x", "Wg", "W1", "W3", "W2", "xd", "h1", "h3", "a", "y", "topk_idx", "gates",
-        "cu_seqlens", "row_of", "tok_of")]
+        "cu_seqlens", "row_of", "tok_of", "logits")]
 
 
 class BwdBufs(C.Structure):

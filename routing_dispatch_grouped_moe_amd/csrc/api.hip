@@ -95,6 +95,8 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.route_part = off;
   off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
   L.route_tickets = off; off = align256(off + (size_t)std::max(L.route_groups, 1) * 4);
+  L.dwg_dense_part = off;
+  off = align256(off + (size_t)dwg_dense_splits(S, H, L.epad) * H * L.epad * 4);
   L.total = off;
   return L;
 }
@@ -290,7 +292,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                           void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(d));
   if (!sv || !b) return MOE_ERR_NULL;
-  if (!(d->flags & MOE_F_RENORM)) return MOE_ERR_UNSUPPORTED;
+  const bool raw = (d->flags & MOE_F_RENORM) == 0;
   if (d->S == 0) {  // no tokens: the weight gradients are zero (or unchanged when accumulating)
     MOE_TRY(check_ptrs({sv->cu_seqlens, dWg, dW1, dW3, dW2}));
     MOE_TRY(check_ws(d, ws, ws_bytes));
@@ -309,6 +311,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                       sv->topk_idx, sv->gates, sv->cu_seqlens, sv->row_of, sv->tok_of}));
   MOE_TRY(check_ptrs({dout, dx, dWg, dW1, dW3, dW2, b->dy, b->dh1, b->dh3, b->dxd, b->dgates,
                       b->dlogits}));
+  if (raw) MOE_TRY(check_ptrs({sv->logits}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -319,8 +322,8 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
   const int H = d->H, Hf = d->Hf, E = d->E, K = d->K;
   float* dl_row = reinterpret_cast<float*>(w + L.dl_row);
 
-  launch_combine_bwd(dout, sv->y, sv->row_of, sv->topk_idx, sv->gates, b->dy, b->dgates, b->dlogits,
-                     dl_row, d->S, H, E, K, R, bf16, s);
+  launch_combine_bwd(dout, sv->y, sv->row_of, sv->topk_idx, sv->gates, raw ? sv->logits : nullptr,
+                     b->dy, b->dgates, b->dlogits, dl_row, d->S, H, E, K, R, bf16, s);
   if (R > 0) {
     launch_tile_table(sv->cu_seqlens, E, L, w, true, s);
     launch_bwd_da(b->dy, sv->cu_seqlens, sv->W2, sv->h1, sv->h3, b->dh1, b->dh3, R, H, Hf, E, L, w,
@@ -335,8 +338,14 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
   launch_bwd_dw13(sv->xd, b->dh1, b->dh3, sv->cu_seqlens, eorder, dW1, dW3, R, H, Hf, E, accum,
                   bf16, s);
   launch_transpose_wg(sv->Wg, w + L.wgT, H, E, L.epad, bf16, false, nullptr, 0, s);
-  launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16, s);
-  launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
+  if (raw) {
+    launch_dx_dense(b->dxd, sv->row_of, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16, s);
+    launch_dwg_dense(sv->x, b->dlogits, dWg, L, w, d->S, H, E, accum, bf16, s);
+  } else {
+    launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16,
+              s);
+    launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
+  }
   return launched();
 }
 

@@ -165,12 +165,13 @@ static int combine_bwd_waves(int H, int piece_el) {
   return nch < 1 ? 1 : (nch > kCbWaves ? kCbWaves : nch);
 }
 
-template <bool BF16, int KT>
+template <bool BF16, int KT, bool RAW>
 __global__ __launch_bounds__(64 * kCbWaves) void combine_bwd_kernel(
     const void* __restrict__ dout, const void* __restrict__ y, const int32_t* __restrict__ row_of,
-    const int32_t* __restrict__ idx, const float* __restrict__ gates, void* __restrict__ dy,
-    float* __restrict__ dgates, float* __restrict__ dlogits, float* __restrict__ dl_row, int S,
-    int H, int E, int K, int64_t R) {
+    const int32_t* __restrict__ idx, const float* __restrict__ gates,
+    const float* __restrict__ logits, void* __restrict__ dy, float* __restrict__ dgates,
+    float* __restrict__ dlogits, float* __restrict__ dl_row, int S, int H, int E, int K,
+    int64_t R) {
   using PC = Piece<BF16>;
   __shared__ float part[kCbWaves][KT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -236,54 +237,83 @@ __global__ __launch_bounds__(64 * kCbWaves) void combine_bwd_kernel(
   float my_dg = 0.f;
   if (lane < K)
     for (int ww = 0; ww < nw; ++ww) my_dg += part[ww][lane];
-  // Renormalised softmax over the chosen experts: dl_k = g_k (dg_k - sum_j g_j dg_j).
-  const float inner = wave_sum(lane < K ? gk * my_dg : 0.f);
-  const float my_dl = gk * (my_dg - inner);
-  if (lane < K) {
-    dgates[(int64_t)s * K + lane] = my_dg;
-    if (rk >= 0) dl_row[rk] = my_dl;
-  }
-  // Dense logit-gradient row: zero off the chosen experts.
+  const float inner = wave_sum(lane < K ? gk * my_dg : 0.f);  // sum_j g_j dg_j
   int ee[KT];
-  float dd[KT];
 #pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    ee[k] = k < K ? __shfl(ek, k, kWave) : -1;
-    dd[k] = __shfl(my_dl, k < K ? k : 0, kWave);
-  }
-  for (int e = lane; e < E; e += 64) {
-    float v = 0.f;
+  for (int k = 0; k < KT; ++k) ee[k] = k < K ? __shfl(ek, k, kWave) : -1;
+  if constexpr (!RAW) {
+    // Renormalised softmax over the chosen experts: dl_k = g_k (dg_k - sum_j g_j dg_j),
+    // zero off the chosen experts.
+    const float my_dl = gk * (my_dg - inner);
+    if (lane < K) {
+      dgates[(int64_t)s * K + lane] = my_dg;
+      if (rk >= 0) dl_row[rk] = my_dl;
+    }
+    float dd[KT];
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-      if (ee[k] == e) v = dd[k];
-    dlogits[(int64_t)s * E + e] = v;
+    for (int k = 0; k < KT; ++k) dd[k] = __shfl(my_dl, k < K ? k : 0, kWave);
+    for (int e = lane; e < E; e += 64) {
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (ee[k] == e) v = dd[k];
+      dlogits[(int64_t)s * E + e] = v;
+    }
+  } else {
+    // Softmax over all E experts, the chosen probabilities used as gates:
+    // dl_e = p_e (dp_e - sum_j g_j dg_j) with dp_e = dg_k where e = idx_k,
+    // else 0; p from the token's logits row (max-shifted, as the router).
+    const float* lrow = logits + (int64_t)s * E;
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, lrow[e]);
+    m = wave_max_f32(m);
+    float z = 0.f;
+    for (int e = lane; e < E; e += 64) z += expf(lrow[e] - m);
+    const float rz = 1.0f / wave_sum(z);
+    float dgk[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) dgk[k] = __shfl(my_dg, k < K ? k : 0, kWave);
+    if (lane < K) dgates[(int64_t)s * K + lane] = my_dg;
+    for (int e = lane; e < E; e += 64) {
+      float dp = 0.f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (ee[k] == e) dp = dgk[k];
+      dlogits[(int64_t)s * E + e] = expf(lrow[e] - m) * rz * (dp - inner);
+    }
   }
 }
 
 template <bool BF16, int KT>
 struct CombineBwdLaunch {
   static void run(const void* dout, const void* y, const int32_t* row_of, const int32_t* idx,
-                  const float* gates, void* dy, float* dgates, float* dlogits, float* dl_row,
-                  int64_t S, int H, int E, int K, int64_t R, hipStream_t s) {
+                  const float* gates, const float* logits, void* dy, float* dgates,
+                  float* dlogits, float* dl_row, int64_t S, int H, int E, int K, int64_t R,
+                  hipStream_t s) {
     const int nw = combine_bwd_waves(H, Piece<BF16>::kEl);
-    hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT>), dim3((unsigned)S), dim3(64 * nw), 0, s,
-                       dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, (int)S, H, E, K,
-                       R);
+    if (logits)
+      hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT, true>), dim3((unsigned)S), dim3(64 * nw),
+                         0, s, dout, y, row_of, idx, gates, logits, dy, dgates, dlogits, dl_row,
+                         (int)S, H, E, K, R);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<BF16, KT, false>), dim3((unsigned)S), dim3(64 * nw),
+                         0, s, dout, y, row_of, idx, gates, logits, dy, dgates, dlogits, dl_row,
+                         (int)S, H, E, K, R);
   }
 };
 
 void launch_combine_bwd(const void* dout, const void* y, const int32_t* row_of,
-                        const int32_t* idx, const float* gates, void* dy, float* dgates,
-                        float* dlogits, float* dl_row, int64_t S, int H, int E, int K, int64_t R,
-                        bool bf16, hipStream_t s) {
+                        const int32_t* idx, const float* gates, const float* logits, void* dy,
+                        float* dgates, float* dlogits, float* dl_row, int64_t S, int H, int E,
+                        int K, int64_t R, bool bf16, hipStream_t s) {
   if (S <= 0) return;
   TimedLaunch tl("combine_bwd", s);
   if (bf16)
-    with_kt<CombineBwdLaunch, true>(K, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row, S,
-                                    H, E, K, R, s);
+    with_kt<CombineBwdLaunch, true>(K, dout, y, row_of, idx, gates, logits, dy, dgates, dlogits,
+                                    dl_row, S, H, E, K, R, s);
   else
-    with_kt<CombineBwdLaunch, false>(K, dout, y, row_of, idx, gates, dy, dgates, dlogits, dl_row,
-                                     S, H, E, K, R, s);
+    with_kt<CombineBwdLaunch, false>(K, dout, y, row_of, idx, gates, logits, dy, dgates, dlogits,
+                                     dl_row, S, H, E, K, R, s);
 }
 
 template <bool BF16, int KT>
@@ -509,6 +539,202 @@ void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* d
     TimedLaunch tl("router_dWg_reduce", s);
     hipLaunchKernelGGL(dwg_reduce_kernel, dim3((H + 63) / 64, (E + 15) / 16), dim3(256), 0, s, part,
                        estart, dWg, H, E, accum ? 1 : 0);
+  }
+}
+
+// ------------------------------------------- router backward, raw softmax --
+// With raw softmax gates every expert's logit has a gradient, so the router
+// terms are dense products over all E experts:
+//   dx[s]  = sum_k dxd[row_of[s*K+k]] + sum_e dl[s,e] Wg[:, e]
+//   dWg    = x^T dl
+// Both are fp32 FMA tiles through LDS (E is small next to H: the products
+// are 2 S H E flops, a few percent of the expert GEMMs).
+
+// Block: 32 tokens x 256 columns; thread (ty, tx) holds tokens 4 ty .. 4 ty + 3
+// and columns 8 tx .. 8 tx + 7; experts in chunks of 16 through LDS (dl as
+// [e][token], the row-major transposed router weight as [e][column]).
+template <bool BF16, int KT>
+__global__ __launch_bounds__(256) void dx_dense_kernel(const void* __restrict__ dxd,
+                                                       const int32_t* __restrict__ row_of,
+                                                       const float* __restrict__ dlogits,
+                                                       const void* __restrict__ wgT,
+                                                       void* __restrict__ dx, int S, int H, int E,
+                                                       int K, int64_t R) {
+  constexpr int TS = 32, TH = 256, TE = 16;
+  __shared__ float sd[TE][TS + 1];
+  __shared__ __attribute__((aligned(16))) float sw[TE][TH];
+  const int s0 = blockIdx.x * TS, h0 = blockIdx.y * TH;
+  const int tid = threadIdx.x, tx = tid & 31, ty = tid >> 5;
+  float acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+  for (int e0 = 0; e0 < E; e0 += TE) {
+    for (int i = tid; i < TS * TE; i += 256) {
+      const int t = i / TE, e = i % TE;
+      sd[e][t] = (s0 + t < S && e0 + e < E) ? dlogits[(int64_t)(s0 + t) * E + e0 + e] : 0.f;
+    }
+    for (int i = tid; i < TE * TH / 8; i += 256) {
+      const int e = i / (TH / 8), c = (i % (TH / 8)) * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (e0 + e < E && h0 + c < H) load8<BF16>(wgT, (int64_t)(e0 + e) * H + h0 + c, v);
+      *reinterpret_cast<float4*>(&sw[e][c]) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(&sw[e][c + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int e = 0; e < TE; ++e) {
+      const float4 w0 = *reinterpret_cast<const float4*>(&sw[e][8 * tx]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sw[e][8 * tx + 4]);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d = sd[e][4 * ty + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(d, w[i], acc[j][i]);
+      }
+    }
+    __syncthreads();
+  }
+  const int h = h0 + 8 * tx;
+  if (h >= H) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = s0 + 4 * ty + j;
+    if (t >= S) continue;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {  // the K dispatched rows, in k order
+      if (k >= K) break;
+      const int r = row_of[(int64_t)t * K + k];
+      if (r < 0 || r >= R) continue;
+      float u[8];
+      load8<BF16>(dxd, (int64_t)r * H + h, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += u[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += acc[j][i];  // then the router term
+    store8<BF16>(dx, (int64_t)t * H + h, v);
+  }
+}
+
+template <bool BF16, int KT>
+struct DxDenseLaunch {
+  static void run(const void* dxd, const int32_t* row_of, const float* dlogits, const void* wgT,
+                  void* dx, int64_t S, int H, int E, int K, int64_t R, hipStream_t s) {
+    hipLaunchKernelGGL((dx_dense_kernel<BF16, KT>), dim3((unsigned)((S + 31) / 32), (H + 255) / 256),
+                       dim3(256), 0, s, dxd, row_of, dlogits, wgT, dx, (int)S, H, E, K, R);
+  }
+};
+
+void launch_dx_dense(const void* dxd, const int32_t* row_of, const float* dlogits,
+                     const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R,
+                     bool bf16, hipStream_t s) {
+  if (S <= 0) return;
+  TimedLaunch tl("dispatch_bwd_dx", s);
+  if (bf16) with_kt<DxDenseLaunch, true>(K, dxd, row_of, dlogits, wgT, dx, S, H, E, K, R, s);
+  else with_kt<DxDenseLaunch, false>(K, dxd, row_of, dlogits, wgT, dx, S, H, E, K, R, s);
+}
+
+// dWg partials: block (256 columns h, 16 experts, token slice z); thread
+// (ty, tx) holds experts 2 ty, 2 ty + 1 of columns 8 tx .. 8 tx + 7, summing
+// the slice's tokens in order; part[z][h][e] (e over epad).
+template <bool BF16>
+__global__ __launch_bounds__(256) void dwg_dense_kernel(const void* __restrict__ x,
+                                                        const float* __restrict__ dlogits,
+                                                        float* __restrict__ part, int S, int H,
+                                                        int E, int epad, int per_split) {
+  constexpr int TS = 32, TH = 256, TE = 16;
+  __shared__ __attribute__((aligned(16))) float sx[TS][TH];
+  __shared__ float sd[TS][TE];
+  const int h0 = blockIdx.x * TH, e0 = blockIdx.y * TE, z = blockIdx.z;
+  const int s_lo = z * per_split, s_hi = min(S, s_lo + per_split);
+  const int tid = threadIdx.x, tx = tid & 31, ty = tid >> 5;
+  float acc[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+  for (int t0 = s_lo; t0 < s_hi; t0 += TS) {
+    for (int i = tid; i < TS * TH / 8; i += 256) {
+      const int t = i / (TH / 8), c = (i % (TH / 8)) * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (t0 + t < s_hi && h0 + c < H) load8<BF16>(x, (int64_t)(t0 + t) * H + h0 + c, v);
+      *reinterpret_cast<float4*>(&sx[t][c]) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(&sx[t][c + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    for (int i = tid; i < TS * TE; i += 256) {
+      const int t = i / TE, e = i % TE;
+      sd[t][e] = (t0 + t < s_hi && e0 + e < E) ? dlogits[(int64_t)(t0 + t) * E + e0 + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int t = 0; t < TS; ++t) {
+      const float4 w0 = *reinterpret_cast<const float4*>(&sx[t][8 * tx]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sx[t][8 * tx + 4]);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const float d0 = sd[t][2 * ty], d1 = sd[t][2 * ty + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[0][i] = fmaf(d0, w[i], acc[0][i]);
+        acc[1][i] = fmaf(d1, w[i], acc[1][i]);
+      }
+    }
+    __syncthreads();
+  }
+  const int h = h0 + 8 * tx;
+  if (h >= H) return;
+  float* o = part + ((size_t)z * H + h) * epad + e0 + 2 * ty;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o[(size_t)i * epad] = acc[0][i];
+    o[(size_t)i * epad + 1] = acc[1][i];
+  }
+}
+
+// dWg[h][e] = (old value under accumulate) + sum over token slices, in order.
+__global__ __launch_bounds__(256) void dwg_dense_reduce_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ dWg, int H,
+                                                               int E, int epad, int nsplit,
+                                                               int accum) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)H * E) return;
+  const int h = (int)(i / E), e = (int)(i % E);
+  float v = 0.f;
+  for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * H + h) * epad + e];
+  dWg[i] = accum ? dWg[i] + v : v;
+}
+
+int dwg_dense_splits(int64_t S, int H, int epad) {
+  const int64_t blocks = (int64_t)((H + 255) / 256) * (epad / 16);
+  int64_t n = blocks >= 256 ? 1 : 256 / blocks;
+  const int64_t chunks = (S + 31) / 32;
+  if (n > chunks) n = chunks;
+  return (int)(n < 1 ? 1 : (n > 64 ? 64 : n));
+}
+
+void launch_dwg_dense(const void* x, const float* dlogits, float* dWg, const WsLayout& L,
+                      char* ws, int64_t S, int H, int E, bool accum, bool bf16, hipStream_t s) {
+  float* part = reinterpret_cast<float*>(ws + L.dwg_dense_part);
+  const int ns = dwg_dense_splits(S, H, L.epad);
+  const int per = (int)(((S + ns - 1) / ns + 31) / 32 * 32);
+  {
+    TimedLaunch tl("router_dWg_partial", s);
+    dim3 grid((H + 255) / 256, L.epad / 16, ns);
+    if (bf16)
+      hipLaunchKernelGGL(dwg_dense_kernel<true>, grid, dim3(256), 0, s, x, dlogits, part, (int)S, H,
+                         E, L.epad, per);
+    else
+      hipLaunchKernelGGL(dwg_dense_kernel<false>, grid, dim3(256), 0, s, x, dlogits, part, (int)S,
+                         H, E, L.epad, per);
+  }
+  {
+    TimedLaunch tl("router_dWg_reduce", s);
+    const int64_t n = (int64_t)H * E;
+    hipLaunchKernelGGL(dwg_dense_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       part, dWg, H, E, L.epad, ns, accum ? 1 : 0);
   }
 }
 

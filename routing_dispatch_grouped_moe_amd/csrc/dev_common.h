@@ -141,6 +141,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
+// Largest value over the wavefront, to every lane (lanes a step leaves out
+// keep their own value).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return fmaxf(v, __uint_as_float(dpp_mov<CTRL, ROWS>(b, b)));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = dpp_fmax<kDppXor1, 0xf>(v);
+  v = dpp_fmax<kDppXor2, 0xf>(v);
+  v = dpp_fmax<kDppHalfMirror, 0xf>(v);
+  v = dpp_fmax<kDppMirror, 0xf>(v);
+  v = dpp_fmax<kDppBcast15, 0xa>(v);
+  v = dpp_fmax<kDppBcast31, 0xc>(v);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);

@@ -35,6 +35,7 @@ struct WsLayout {
   size_t gemm_part;   // [tail_items, 256 * 256] fp32 K-split partial tiles of the last GEMM wave
   size_t route_part;  // [groups, route_parts, 32, epad] fp32 partial logits of a split router
   size_t route_tickets; // [groups] int32 parts finished per 32-token group
+  size_t dwg_dense_part; // [splits, H, epad] fp32 token-slice partials of the dense dWg (raw gates)
   size_t total;
   int nb;             // dispatch blocks of 256 tokens
   int epad;           // E rounded up to 16
@@ -96,13 +97,22 @@ void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int
 
 void launch_combine(const void* y, const int32_t* row_of, const float* gates, void* out, int64_t S,
                     int H, int K, int64_t R, bool bf16, hipStream_t s);
+// logits [S, E] given: raw softmax gates (dlogits dense over all experts);
+// nullptr: gates renormalised over the K chosen
 void launch_combine_bwd(const void* dout, const void* y, const int32_t* row_of,
-                        const int32_t* idx, const float* gates, void* dy, float* dgates,
-                        float* dlogits, float* dl_row, int64_t S, int H, int E, int K, int64_t R,
-                        bool bf16, hipStream_t s);
+                        const int32_t* idx, const float* gates, const float* logits, void* dy,
+                        float* dgates, float* dlogits, float* dl_row, int64_t S, int H, int E,
+                        int K, int64_t R, bool bf16, hipStream_t s);
 void launch_dx(const void* dxd, const int32_t* row_of, const int32_t* idx, const float* dlogits,
                const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R, bool bf16,
                hipStream_t s);
+// raw softmax gates: the router terms are dense over all experts
+void launch_dx_dense(const void* dxd, const int32_t* row_of, const float* dlogits,
+                     const void* wgT, void* dx, int64_t S, int H, int E, int K, int64_t R,
+                     bool bf16, hipStream_t s);
+int dwg_dense_splits(int64_t S, int H, int epad);
+void launch_dwg_dense(const void* x, const float* dlogits, float* dWg, const WsLayout& L,
+                      char* ws, int64_t S, int H, int E, bool accum, bool bf16, hipStream_t s);
 void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* dWg,
                 const WsLayout& L, char* ws, int64_t R, int H, int E, bool accum, bool bf16,
                 hipStream_t s);

@@ -81,7 +81,7 @@ class MoELayer:
     def backward(self, dout, x, Wg, W1, W3, W2):
         saved = dict(x=x, Wg=Wg, W1=W1, W3=W3, W2=W2, xd=self.xd, h1=self.h1, h3=self.h3, a=self.a,
                      y=self.y, topk_idx=self.topk_idx, gates=self.gates, cu_seqlens=self.cu,
-                     row_of=self.row_of, tok_of=self.tok_of)
+                     row_of=self.row_of, tok_of=self.tok_of, logits=self.logits)
         bufs = dict(dy=self.dy, dh1=self.dh1, dh3=self.dh3, dxd=self.dxd, dgates=self.dgates,
                     dlogits=self.dlogits)
         L.moe_backward(self.d, saved, dout, self.dx, self.dWg, self.dW1, self.dW3, self.dW2, bufs,

@@ -99,12 +99,12 @@ def test_other_entry_points_reject_before_launch(L):
     assert lib.moe_combine(C.byref(d), FAKE, FAKE, None, FAKE, None) == 1
     dshape = L.dims(64, 192, 256, 8, 2, "bf16")
     assert lib.moe_combine(C.byref(dshape), FAKE, FAKE, FAKE, FAKE, None) == 6
-    # backward: raw (non-renormalised) gating is not implemented on the device
-    sv = L.Saved(*([1 << 20] * 15))
+    # backward: raw (non-renormalised) gates need the saved logits
+    sv = L.Saved(*([1 << 20] * 15 + [0]))
     bb = L.BwdBufs(*([1 << 20] * 6))
     draw = L.dims(64, 128, 256, 8, 2, "bf16", flags=0)
     assert lib.moe_backward(C.byref(draw), C.byref(sv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            C.byref(bb), FAKE, ws_n, None) == 6
+                            C.byref(bb), FAKE, ws_n, None) == 1
     assert lib.moe_backward(C.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(bb), FAKE,
                             ws_n, None) == 1
     sv_bad = L.Saved(*([1 << 20] * 14 + [0]))

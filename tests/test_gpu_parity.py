@@ -33,7 +33,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True):
+def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True, flags=L.MOE_F_RENORM):
     """Upload a workload, run the GPU forward (+ backward); return host copies."""
     dt = wl.dtype
     x = to_dev(wl.x, dt)
@@ -41,7 +41,7 @@ def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True):
     b = None if wl.bias is None else torch.from_numpy(wl.bias.astype(np.float32)).cuda()
     W1 = to_dev(wl.W1, dt); W3 = to_dev(wl.W3, dt); W2 = to_dev(wl.W2, dt)
     dout = to_dev(wl.dout, dt)
-    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt)
+    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt, flags=flags)
     L.moe_clear_status(layer.ws)
     layer.forward(x, Wg, b, W1, W3, W2)
     if backward:
@@ -56,13 +56,14 @@ def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True):
     return got
 
 
-def check_against_oracle(wl, got, tol, backward=True):
+def check_against_oracle(wl, got, tol, backward=True, renorm=True):
     x, Wg, bias = wl.x, wl.Wg, wl.bias
     S, E, K = wl.S, wl.E, wl.K
     # router logits: fp32 accumulation on both sides
     want_logits = oracle.router_logits(x, Wg, bias)
     assert_close("logits", got["logits"], want_logits, 1e-5)
-    fw, bw = oracle_on_gpu_routing(x, Wg, bias, wl.W1, wl.W3, wl.W2, K, got["logits"], wl.dout)
+    fw, bw = oracle_on_gpu_routing(x, Wg, bias, wl.W1, wl.W3, wl.W2, K, got["logits"], wl.dout,
+                                   renorm=renorm)
     np.testing.assert_array_equal(got["topk_idx"], fw["idx"], err_msg="topk_idx")
     assert_close("gates", got["gates"], fw["gates"], 1e-5)
     np.testing.assert_array_equal(got["counts"], fw["counts"], err_msg="counts")
@@ -121,6 +122,32 @@ def test_layer_parity(cid, cfg, ov):
     assert got["status"] == 0
     if wl.dtype == "f32":
         assert flips == 0
+
+
+# Raw softmax gates (the chosen entries of the softmax over all E experts, no
+# renormalisation): dense dlogits, and the router terms of dx and dWg over
+# every expert.
+RAW_CASES = [
+    ("c1_tiny_fp32_raw", "c1", {}),
+    ("c2_mixtral_shape_raw", "c2", dict(S=300, H=256, Hf=384)),
+    ("c3_zipf_raw", "c3", dict(S=257, H=256, Hf=256)),
+    ("c4_moonep_skewed_raw", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
+]
+
+
+@pytest.mark.parametrize("cid,cfg,ov", RAW_CASES, ids=[c[0] for c in RAW_CASES])
+def test_layer_parity_raw_gates(cid, cfg, ov):
+    _say(f"[parity raw] {cid}: {cfg} {ov}")
+    wl = make_workload(cfg, host_weights=True, **ov)
+    got = run_layer(wl, flags=0)
+    assert got["status"] == 0
+    tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
+    errs, flips = check_against_oracle(wl, got, tol, renorm=False)
+    # raw gates do not sum to one; dlogits is non-zero off the chosen experts
+    assert np.all(got["gates"].sum(axis=1) < 1.0 + 1e-6)
+    assert np.count_nonzero(got["dlogits"]) > got["topk_idx"].size
+    _say(f"[parity raw] {cid}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
+         + f" flips={flips}")
 
 
 @pytest.mark.parametrize("cfg,ov", [("c3", dict(S=257, H=256, Hf=256)),
