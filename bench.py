@@ -51,6 +51,11 @@ def kernel_model(name, cfg, counts):
         "dispatch_bwd_dx": (2 * R * H, R * H * b + S * H * b + E * H * b + 8 * S * K),
         "router_dWg_partial": (2 * R * H, R * H * b + 4 * R),
     }
+    if cfg.get("raw"):
+        # raw softmax gates: dense dlogits, router terms over all E experts
+        m["combine_bwd"] = (4 * R * H + 8 * S * E, S * H * b + 2 * R * H * b + 8 * S * E + 4 * S * K)
+        m["dispatch_bwd_dx"] = (2 * S * H * E + R * H, R * H * b + S * H * b + E * H * b + 4 * S * E)
+        m["router_dWg_partial"] = (2 * S * H * E, S * H * b + 4 * S * E)
     return m.get(name)
 
 
@@ -157,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None)
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    ap.add_argument("--gates", default="renorm", choices=["renorm", "raw"],
+                    help="gates renormalised over the K chosen experts (default) or raw softmax")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size kernel for "
                          "scaling HBM traffic counters)")
@@ -191,16 +198,18 @@ def main():
     bias = None if wl.bias is None else torch.from_numpy(wl.bias).to(dev)
     W1, W3, W2 = device_expert_weights(cfg, dev)
     mod = "B" in cfg
+    flags = L.MOE_F_RENORM if args.gates == "renorm" else 0
     if mod:
         w_r = up(wl.w_r)
-        layer = MoDMoELayer(cfg["B"], cfg["T"], cfg["C"], wl.H, wl.Hf, wl.E, wl.K, wl.dtype, dev)
+        layer = MoDMoELayer(cfg["B"], cfg["T"], cfg["C"], wl.H, wl.Hf, wl.E, wl.K, wl.dtype, dev,
+                            flags=flags)
         moe = layer.moe
 
         def step():
             layer.forward(x, w_r, Wg, bias, W1, W3, W2)
             layer.backward(dout, x, w_r, Wg, W1, W3, W2)
     else:
-        layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, wl.dtype, dev)
+        layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, wl.dtype, dev, flags=flags)
         moe = layer
 
         def step():
@@ -242,7 +251,8 @@ def main():
     counts = moe.counts.cpu().numpy().tolist()
     c = np.asarray(counts, np.float64)
     maxvio = float(c.max() / c.mean() - 1.0)
-    mcfg = dict(S=moe.S, H=wl.H, Hf=wl.Hf, E=wl.E, K=wl.K, dtype=wl.dtype)
+    mcfg = dict(S=moe.S, H=wl.H, Hf=wl.Hf, E=wl.E, K=wl.K, dtype=wl.dtype,
+                raw=args.gates == "raw")
 
     kernels = {}
     for name, (ms, n) in sorted(ktab.items(), key=lambda kv: -kv[1][0]):
@@ -283,7 +293,9 @@ def main():
         "config": {"workload": cfg["workload"], "tokens": S_in, "moe_tokens": moe.S, "H": wl.H,
                    "H_ffn": wl.Hf, "experts": wl.E, "top_k": wl.K, "router_bias_beta": wl.beta,
                    "maxvio_measured": maxvio, "parallelism": "single GPU, all experts resident",
-                   "step": "forward" if fwd_only else "forward+backward"},
+                   "step": "forward" if fwd_only else "forward+backward",
+                   "gates": "softmax renormalised over the top-K" if args.gates == "renorm"
+                   else "raw softmax (no renormalisation)"},
         "roofline": roof,
         "grouped_gemm_mfma_frac": (gflops / gtime) / PEAK_BF16 if gtime > 0 else None,
         "grouped_gemm_hbm_frac": (

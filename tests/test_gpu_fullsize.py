@@ -80,13 +80,29 @@ FULL = [
 
 @pytest.mark.parametrize("cid,cfg,maxvio", FULL, ids=[c[0] for c in FULL])
 def test_fullsize_sampled(cid, cfg, maxvio):
+    run_fullsize(cid, cfg, maxvio)
+
+
+# raw softmax gates at full size (dense dlogits and router terms)
+FULL_RAW = [
+    ("c2_mixtral_full_raw", "c2", None),
+    ("c4_moonep_full_raw_maxvio20", "c4", 20.0),
+]
+
+
+@pytest.mark.parametrize("cid,cfg,maxvio", FULL_RAW, ids=[c[0] for c in FULL_RAW])
+def test_fullsize_sampled_raw_gates(cid, cfg, maxvio):
+    run_fullsize(cid, cfg, maxvio, renorm=False)
+
+
+def run_fullsize(cid, cfg, maxvio, renorm=True):
     _say(f"[full] {cid}: building inputs")
     wl = make_workload(cfg, maxvio=maxvio, host_weights=False)
     S, H, Hf, E, K = wl.S, wl.H, wl.Hf, wl.E, wl.K
     x_t, Wg_t, dout_t = to_dev(wl.x, "bf16"), to_dev(wl.Wg, "bf16"), to_dev(wl.dout, "bf16")
     bias_t = None if wl.bias is None else torch.from_numpy(wl.bias.astype(np.float32)).cuda()
     W1, W3, W2 = device_expert_weights(wl.cfg, "cuda")
-    layer = MoELayer(S, H, Hf, E, K, "bf16")
+    layer = MoELayer(S, H, Hf, E, K, "bf16", flags=L.MOE_F_RENORM if renorm else 0)
     L.moe_clear_status(layer.ws)
     _say(f"[full] {cid}: forward + backward S={S} H={H} H'={Hf} E={E} K={K}")
     layer.forward(x_t, Wg_t, bias_t, W1, W3, W2)
@@ -94,10 +110,10 @@ def test_fullsize_sampled(cid, cfg, maxvio):
     torch.cuda.synchronize()
     assert layer.status() == 0
     check_moe_sampled(cid, layer, wl.x, x_t, wl.dout, wl.Wg, wl.bias, W1, W3, W2,
-                      np.random.default_rng(12345))
+                      np.random.default_rng(12345), renorm=renorm)
 
 
-def check_moe_sampled(cid, layer, x, x_t, dout, Wg, bias, W1, W3, W2, rng):
+def check_moe_sampled(cid, layer, x, x_t, dout, Wg, bias, W1, W3, W2, rng, renorm=True):
     """Check a finished MoELayer forward + backward against the oracle (sampled as above).
 
     x / dout: the layer's input and upstream gradient on the host (exact
@@ -111,7 +127,7 @@ def check_moe_sampled(cid, layer, x, x_t, dout, Wg, bias, W1, W3, W2, rng):
     assert_close("logits[sample]", logits[ts], oracle.router_logits(x[ts], Wg, bias), F32_TOL)
     idx = oracle.topk_experts(logits, K)
     np.testing.assert_array_equal(to_host(layer.topk_idx), idx, err_msg="topk_idx")
-    gates = oracle.gate_weights(logits, idx)
+    gates = oracle.gate_weights(logits, idx, renorm=renorm)
     assert_close("gates", to_host(layer.gates), gates, F32_TOL)
     counts, cu = oracle.expert_counts(idx, E)
     np.testing.assert_array_equal(to_host(layer.counts), counts, err_msg="counts")
@@ -166,7 +182,7 @@ def check_moe_sampled(cid, layer, x, x_t, dout, Wg, bias, W1, W3, W2, rng):
     rows_t = torch.from_numpy(all_rows).cuda()
     assert_close("dy[rows]", to_host(layer.dy[rows_t]), dy_s, BF16_TOL)
     assert_close("dgates[tokens]", to_host(layer.dgates)[toks], dg, BF16_TOL)
-    dl = oracle.gate_backward(dg, logits[toks], idx[toks])
+    dl = oracle.gate_backward(dg, logits[toks], idx[toks], renorm=renorm)
     dl_gpu = to_host(layer.dlogits)
     assert_close("dlogits[tokens]", dl_gpu[toks], dl, BF16_TOL)
 
