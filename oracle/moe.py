@@ -343,3 +343,24 @@ def maxvio(counts):
     """max_e counts[e] / mean(counts) - 1 ([MEP] "Which problem MoonEP solves": 0 is perfect balance)."""
     c = np.asarray(counts, dtype=F64)
     return float(c.max() / c.mean() - 1.0)
+
+
+def load_entropy(counts):
+    """-sum_e f_e ln f_e over the experts with f_e = counts[e] / sum(counts) > 0 (natural log).
+
+    A second load statistic of the routing histogram next to maxvio ([MEP]
+    "Which problem MoonEP solves": the per-expert load the dispatch must
+    absorb): ln E for a perfectly balanced load, 0 when one expert takes
+    every pair.  The pages name no formula; this is the Shannon entropy of
+    the load distribution.
+    """
+    c = np.asarray(counts, dtype=F64)
+    tot = c.sum()
+    if tot == 0:
+        return 0.0
+    h = 0.0
+    for v in c:
+        if v > 0:
+            f = v / tot
+            h -= f * np.log(f)
+    return float(h)

@@ -163,3 +163,19 @@ def test_dispatch_invariants_and_comparison_sort(S, E, K):
 def test_maxvio_definition():
     assert oracle.maxvio([4, 4, 4, 4]) == 0.0
     assert oracle.maxvio([16, 0, 0, 0]) == pytest.approx(3.0)
+
+
+def test_load_entropy_closed_forms():
+    # balanced load: ln E; one expert takes every pair: 0; a 3:1 split of two
+    # experts: ln 4 - (3/4) ln 3 (worked by hand: -(3/4) ln(3/4) - (1/4) ln(1/4))
+    assert oracle.load_entropy([5, 5, 5, 5, 5, 5, 5, 5]) == pytest.approx(np.log(8), rel=1e-14)
+    assert oracle.load_entropy([0, 0, 12, 0]) == 0.0
+    assert oracle.load_entropy([3, 0, 1]) == pytest.approx(np.log(4) - 0.75 * np.log(3), rel=1e-14)
+    assert oracle.load_entropy([0, 0, 0]) == 0.0
+    # invariant under relabelling the experts and under scaling every count
+    rng = np.random.default_rng(3)
+    c = rng.integers(0, 50, size=37)
+    assert oracle.load_entropy(c) == pytest.approx(oracle.load_entropy(rng.permutation(c)), rel=1e-13)
+    assert oracle.load_entropy(c) == pytest.approx(oracle.load_entropy(7 * c), rel=1e-13)
+    # between 0 and ln(#experts with load)
+    assert 0.0 <= oracle.load_entropy(c) <= np.log(np.count_nonzero(c)) + 1e-12
