@@ -274,6 +274,19 @@ moe_status_t moe_mod_backward(int32_t B, int32_t T, int32_t C, int32_t H, int32_
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_load_stats - load statistics of a routing histogram ([MEP] "Which
+ * problem MoonEP solves": maxvio, the most loaded expert's load over the
+ * mean load, minus one).
+ *   counts [E] int32 device (moe_route's per-expert counts)
+ *   stats  [2] fp32 device output: stats[0] = maxvio = max_e c_e / mean_e c_e - 1,
+ *          stats[1] = load entropy = -sum_e f_e ln f_e over f_e = c_e / sum c > 0
+ *          (ln E when balanced, 0 when one expert takes every pair); both 0
+ *          when every count is 0.
+ * 1 <= E <= 1024.  Asynchronous on `stream`; no workspace.
+ */
+moe_status_t moe_load_stats(int32_t E, const int32_t* counts, float* stats, void* stream);
+
+/*
  * Optional per-kernel timer (measurement only).  When enabled, every kernel
  * the library launches is bracketed by a pair of hipEvents recorded on the
  * stream it is launched on; moe_timer_read sums the elapsed milliseconds and

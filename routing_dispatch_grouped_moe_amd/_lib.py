@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 # Every entry point include/moe.h declares (checked by the CPU test suite).
 EXPORTS = (
     "moe_workspace_bytes", "moe_clear_status", "moe_status_string", "moe_read_status",
-    "moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_ffn_up", "moe_ffn_down",
+    "moe_route", "moe_load_stats", "moe_dispatch", "moe_grouped_ffn", "moe_ffn_up", "moe_ffn_down",
     "moe_combine", "moe_backward", "moe_mod_workspace_bytes", "moe_mod_select",
     "moe_mod_merge", "moe_mod_backward", "moe_timer_enable", "moe_timer_reset",
     "moe_timer_read",
@@ -75,6 +75,7 @@ def load():
         "moe_read_status": (I32, [P, C.POINTER(U32), P]),
         "moe_route": (I32, [D, P, P, P, P, P, P, P, P, S, P]),
         "moe_dispatch": (I32, [D, P, P, P, P, P, P, P, S, P]),
+        "moe_load_stats": (I32, [I32, P, P, P]),
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_ffn_up": (I32, [D, P, P, P, P, P, P, P, P, S, P]),
         "moe_ffn_down": (I32, [D, P, P, P, P, P, S, P]),
@@ -135,6 +136,11 @@ def moe_route(d, x, Wg, bias, logits, topk_idx, gates, counts, ws):
     _check("moe_route", load().moe_route(C.byref(d), _p(x), _p(Wg), _p(bias), _p(logits),
                                          _p(topk_idx), _p(gates), _p(counts), _p(ws),
                                          ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_load_stats(E, counts, stats):
+    """stats [2] fp32 (device) <- (maxvio, load entropy) of the counts [E] int32 (device)."""
+    _check("moe_load_stats", load().moe_load_stats(int(E), _p(counts), _p(stats), _stream()))
 
 
 def moe_dispatch(d, x, topk_idx, cu_seqlens, row_of, tok_of, xd, ws):

@@ -208,6 +208,15 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   return launched();
 }
 
+moe_status_t moe_load_stats(int32_t E, const int32_t* counts, float* stats, void* stream) {
+  if (E < 1 || E > 1024) return MOE_ERR_SHAPE;
+  if (!counts || !stats) return MOE_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(counts) & 3u) || (reinterpret_cast<uintptr_t>(stats) & 3u))
+    return MOE_ERR_ALIGN;
+  launch_load_stats(counts, E, stats, reinterpret_cast<hipStream_t>(stream));
+  return launched();
+}
+
 moe_status_t moe_dispatch(const moe_dims_t* d, const void* x, const int32_t* topk_idx,
                           int32_t* cu_seqlens, int32_t* row_of, int32_t* tok_of, void* xd,
                           void* ws, size_t ws_bytes, void* stream) {

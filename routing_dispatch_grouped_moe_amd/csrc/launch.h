@@ -65,6 +65,8 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
                   int K, bool renorm, bool bf16, int nparts, float* rpart, int32_t* tickets,
                   hipStream_t s);
 
+void launch_load_stats(const int32_t* counts, int E, float* stats, hipStream_t s);
+
 void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
                      int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
                      int E, int K, bool bf16, hipStream_t s);

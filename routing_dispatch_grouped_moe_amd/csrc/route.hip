@@ -512,4 +512,34 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
 #undef ROUTE_CASE
 }
 
+// Load statistics of the routing histogram: one block of 1024 threads, one
+// expert each; the sums and the maximum meet through the wavefront
+// reductions and LDS in a fixed order (deterministic).
+__global__ __launch_bounds__(1024) void load_stats_kernel(const int32_t* __restrict__ counts,
+                                                          int E, float* __restrict__ stats) {
+  __shared__ float part[3][16];
+  const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+  const float c = e < E ? (float)max(counts[e], 0) : 0.f;
+  const float tot = wave_sum(c), mx = wave_max_f32(c);
+  if (lane == 0) { part[0][w] = tot; part[1][w] = mx; }
+  __syncthreads();
+  float total = 0.f, cmax = 0.f;
+  for (int i = 0; i < 16; ++i) { total += part[0][i]; cmax = fmaxf(cmax, part[1][i]); }
+  const float f = total > 0.f ? c / total : 0.f;
+  const float h = wave_sum(f > 0.f ? -f * logf(f) : 0.f);
+  if (lane == 0) part[2][w] = h;
+  __syncthreads();
+  if (e == 0) {
+    float ent = 0.f;
+    for (int i = 0; i < 16; ++i) ent += part[2][i];
+    stats[0] = total > 0.f ? cmax * (float)E / total - 1.0f : 0.f;
+    stats[1] = ent;
+  }
+}
+
+void launch_load_stats(const int32_t* counts, int E, float* stats, hipStream_t s) {
+  TimedLaunch tl("load_stats", s);
+  hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(1024), 0, s, counts, E, stats);
+}
+
 }  // namespace moe

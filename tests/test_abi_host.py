@@ -110,6 +110,10 @@ def test_other_entry_points_reject_before_launch(L):
     sv_bad = L.Saved(*([1 << 20] * 14 + [0]))
     assert lib.moe_backward(C.byref(d), C.byref(sv_bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             C.byref(bb), FAKE, ws_n, None) == 1
+    # load statistics
+    assert lib.moe_load_stats(0, FAKE, FAKE, None) == 2
+    assert lib.moe_load_stats(1025, FAKE, FAKE, None) == 2
+    assert lib.moe_load_stats(8, None, FAKE, None) == 1
     # MoD
     assert lib.moe_mod_select(4, 2048, 3000, 4096, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6
     assert lib.moe_mod_select(4, 10000, 10, 4096, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6

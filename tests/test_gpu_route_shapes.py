@@ -7,7 +7,8 @@ accumulate exact bf16 products in at least fp32), the top-K bit for bit
 against the oracle's selection on the GPU's own fp32 logits (the integer
 decision taken in the same precision), gates to 1e-5 and per-expert counts
 bit for bit.  S = 100 leaves a ragged last block of 4 tokens.  A second test
-runs token counts on both sides of the H-split rule (split up to 1024 tokens).
+runs token counts on both sides of the H-split rule (split up to 1024 tokens);
+a third checks the load statistics of routing histograms (maxvio, load entropy).
 """
 import sys
 
@@ -92,3 +93,30 @@ def test_route_split_boundary(S, H, E, K):
     assert_close("gates", to_host(gates), oracle.gate_weights(got_l, want_idx), F32_TOL)
     want_counts, _ = oracle.expert_counts(want_idx, E)
     np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
+
+
+def test_load_stats():
+    """maxvio and load entropy of routing histograms through the C ABI against the oracle."""
+    rng = np.random.default_rng(5)
+    cases = {
+        "balanced": np.full(384, 171, np.int32),
+        "one_hot": np.eye(1, 64, 17, dtype=np.int32)[0] * 8192,
+        "zipf": np.floor(8192 * 4 / np.arange(1, 65) ** 1.1 / np.sum(1 / np.arange(1, 65) ** 1.1))
+        .astype(np.int32),
+        "random": rng.integers(0, 1000, size=1000).astype(np.int32),
+        "single_expert": np.array([5], np.int32),
+        "all_zero": np.zeros(16, np.int32),
+    }
+    for name, c in cases.items():
+        print(f"[load stats] {name} E={c.size}", flush=True)
+        ct = torch.from_numpy(c).cuda()
+        st = torch.full((2,), -1.0, dtype=torch.float32, device="cuda")
+        L.moe_load_stats(c.size, ct, st)
+        torch.cuda.synchronize()
+        got = st.cpu().numpy()
+        if c.sum() == 0:
+            assert got.tolist() == [0.0, 0.0]
+            continue
+        np.testing.assert_allclose(got[0], oracle.maxvio(c), rtol=1e-5, atol=1e-6, err_msg=name)
+        np.testing.assert_allclose(got[1], oracle.load_entropy(c), rtol=1e-5, atol=1e-6,
+                                   err_msg=name)
