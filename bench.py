@@ -164,6 +164,8 @@ def main():
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
     ap.add_argument("--gates", default="renorm", choices=["renorm", "raw"],
                     help="gates renormalised over the K chosen experts (default) or raw softmax")
+    ap.add_argument("--recompute", action="store_true",
+                    help="keep no h1/h3 between forward and backward (the backward recomputes them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size kernel for "
                          "scaling HBM traffic counters)")
@@ -198,7 +200,8 @@ def main():
     bias = None if wl.bias is None else torch.from_numpy(wl.bias).to(dev)
     W1, W3, W2 = device_expert_weights(cfg, dev)
     mod = "B" in cfg
-    flags = L.MOE_F_RENORM if args.gates == "renorm" else 0
+    flags = (L.MOE_F_RENORM if args.gates == "renorm" else 0) | \
+        (L.MOE_F_RECOMPUTE if args.recompute else 0)
     if mod:
         w_r = up(wl.w_r)
         layer = MoDMoELayer(cfg["B"], cfg["T"], cfg["C"], wl.H, wl.Hf, wl.E, wl.K, wl.dtype, dev,
@@ -277,6 +280,13 @@ def main():
                 for n in gemm_names if n in kernels)
     disp = kernels.get("dispatch_scatter", {})
 
+    # device memory the layer holds: all its buffers, and the part the
+    # forward leaves for the backward (inputs excluded)
+    def nbytes(t):
+        return 0 if t is None else t.numel() * t.element_size()
+    kept = sum(nbytes(getattr(moe, n, None)) for n in
+               ("logits", "topk_idx", "gates", "cu", "row_of", "tok_of", "xd", "h1", "h3", "a", "y"))
+    held = sum(nbytes(v) for v in vars(moe).values() if isinstance(v, torch.Tensor))
     out = {
         "metric": METRIC_FWD if fwd_only else METRIC,
         "value": S_in * args.steps / elapsed,
@@ -295,7 +305,11 @@ def main():
                    "maxvio_measured": maxvio, "parallelism": "single GPU, all experts resident",
                    "step": "forward" if fwd_only else "forward+backward",
                    "gates": "softmax renormalised over the top-K" if args.gates == "renorm"
-                   else "raw softmax (no renormalisation)"},
+                   else "raw softmax (no renormalisation)",
+                   "activations": "h1, h3 recomputed in the backward" if args.recompute
+                   else "h1, h3 saved"},
+        "memory": {"layer_buffers_gb": held / 1e9, "kept_forward_to_backward_gb": kept / 1e9,
+                   "peak_allocated_gb": torch.cuda.max_memory_allocated(dev) / 1e9},
         "roofline": roof,
         "grouped_gemm_mfma_frac": (gflops / gtime) / PEAK_BF16 if gtime > 0 else None,
         "grouped_gemm_hbm_frac": (

@@ -73,7 +73,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 /* dims.flags */
 enum {
   MOE_F_RENORM = 1u << 0,     /* gates renormalised over the K chosen experts (Mixtral block) */
-  MOE_F_ACCUM_GRAD = 1u << 1  /* weight gradients are added to (not written over) dW, dWg */
+  MOE_F_ACCUM_GRAD = 1u << 1, /* weight gradients are added to (not written over) dW, dWg */
+  MOE_F_RECOMPUTE = 1u << 3   /* h1, h3 are not kept: the forward writes only a, the backward
+                                 recomputes h1, h3 into its dh1, dh3 buffers (see moe_backward) */
 };
 
 /* Device-side status bits (OR-ed into the workspace status word). */
@@ -161,7 +163,8 @@ moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const int32_t* 
  *   cu_seqlens [E+1]       int32 row offsets (from moe_dispatch)
  *   W1, W3     [E, H, Hf]  gate and up projections (dtype)
  *   W2         [E, Hf, H]  down projection (dtype)
- *   h1, h3     [R, Hf]     outputs: xd*W1[e], xd*W3[e] (dtype; saved for backward)
+ *   h1, h3     [R, Hf]     outputs: xd*W1[e], xd*W3[e] (dtype; saved for backward);
+ *                          not written, and may be NULL, under MOE_F_RECOMPUTE
  *   a          [R, Hf]     output: silu(h1)*h3, from the fp32 values (dtype)
  *   y          [R, H]      output: a*W2[e] (dtype)
  * Equivalent to moe_ffn_up followed by moe_ffn_down.
@@ -237,6 +240,11 @@ typedef struct {
  * dlogits[s, e] = p_e (dp_e - sum_k g_k dg_k) is dense over all experts,
  * saved->logits is required (MOE_ERR_NULL otherwise), and dx's router term
  * and dWg are dense products over all E.
+ * With MOE_F_RECOMPUTE the forward did not keep h1, h3 (saved->h1, h3 may be
+ * NULL): the backward recomputes them from xd into bufs->dh1, dh3 (one more
+ * up-projection GEMM) and the SwiGLU backward overwrites them there in
+ * place; results are bitwise those of the saving mode ([FW] "What's in the
+ * box", sparse-backward item: gradients without saving intermediates).
  */
 moe_status_t moe_backward(const moe_dims_t* dims, const moe_saved_t* saved, const void* dout,
                           void* dx, float* dWg, float* dW1, float* dW3, float* dW2,

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_F_RENORM, MOE_F_ACCUM_GRAD = 1, 2
+MOE_F_RENORM, MOE_F_ACCUM_GRAD, MOE_F_RECOMPUTE = 1, 2, 8
 MOE_DEV_NONFINITE_LOGIT, MOE_DEV_BAD_EXPERT, MOE_DEV_DUP_EXPERT = 1, 2, 4
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
                 4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED",

@@ -236,7 +236,9 @@ moe_status_t moe_ffn_up(const moe_dims_t* d, const void* xd, const int32_t* cu, 
                         void* stream) {
   MOE_TRY(check_dims(d));
   if (d->S == 0) return MOE_OK;
-  MOE_TRY(check_ptrs({xd, cu, W1, W3, h1, h3, a}));
+  const bool keep_h = (d->flags & MOE_F_RECOMPUTE) == 0;
+  MOE_TRY(check_ptrs({xd, cu, W1, W3, a}));
+  if (keep_h) MOE_TRY(check_ptrs({h1, h3}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -244,7 +246,8 @@ moe_status_t moe_ffn_up(const moe_dims_t* d, const void* xd, const int32_t* cu, 
   const int64_t R = d->S * d->K;
   if (R > 0) {
     launch_tile_table(cu, d->E, L, w, false, s);
-    launch_ffn_up(xd, cu, W1, W3, h1, h3, a, R, d->H, d->Hf, d->E, L, w, d->dtype == MOE_BF16, s);
+    launch_ffn_up(xd, cu, W1, W3, keep_h ? h1 : nullptr, keep_h ? h3 : nullptr, a, R, d->H, d->Hf,
+                  d->E, L, w, d->dtype == MOE_BF16, s);
   }
   return launched();
 }
@@ -271,7 +274,9 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* d, const void* xd, const int32_t*
                              void* a, void* y, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(d));
   if (d->S == 0) return MOE_OK;
-  MOE_TRY(check_ptrs({xd, cu, W1, W3, W2, h1, h3, a, y}));
+  const bool keep_h = (d->flags & MOE_F_RECOMPUTE) == 0;
+  MOE_TRY(check_ptrs({xd, cu, W1, W3, W2, a, y}));
+  if (keep_h) MOE_TRY(check_ptrs({h1, h3}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -280,7 +285,8 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* d, const void* xd, const int32_t*
   const int64_t R = d->S * d->K;
   if (R > 0) {
     launch_tile_table(cu, d->E, L, w, false, s);
-    launch_ffn_up(xd, cu, W1, W3, h1, h3, a, R, d->H, d->Hf, d->E, L, w, bf16, s);
+    launch_ffn_up(xd, cu, W1, W3, keep_h ? h1 : nullptr, keep_h ? h3 : nullptr, a, R, d->H, d->Hf,
+                  d->E, L, w, bf16, s);
     launch_ffn_down(a, cu, W2, y, R, d->H, d->Hf, d->E, L, w, bf16, s);
   }
   return launched();
@@ -316,8 +322,10 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                d->E, accum, bf16, s);
     return launched();
   }
-  MOE_TRY(check_ptrs({sv->x, sv->Wg, sv->W1, sv->W3, sv->W2, sv->xd, sv->h1, sv->h3, sv->a, sv->y,
-                      sv->topk_idx, sv->gates, sv->cu_seqlens, sv->row_of, sv->tok_of}));
+  const bool recompute = (d->flags & MOE_F_RECOMPUTE) != 0;
+  MOE_TRY(check_ptrs({sv->x, sv->Wg, sv->W1, sv->W3, sv->W2, sv->xd, sv->a, sv->y, sv->topk_idx,
+                      sv->gates, sv->cu_seqlens, sv->row_of, sv->tok_of}));
+  if (!recompute) MOE_TRY(check_ptrs({sv->h1, sv->h3}));
   MOE_TRY(check_ptrs({dout, dx, dWg, dW1, dW3, dW2, b->dy, b->dh1, b->dh3, b->dxd, b->dgates,
                       b->dlogits}));
   if (raw) MOE_TRY(check_ptrs({sv->logits}));
@@ -335,8 +343,18 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                      b->dy, b->dgates, b->dlogits, dl_row, d->S, H, E, K, R, bf16, s);
   if (R > 0) {
     launch_tile_table(sv->cu_seqlens, E, L, w, true, s);
-    launch_bwd_da(b->dy, sv->cu_seqlens, sv->W2, sv->h1, sv->h3, b->dh1, b->dh3, R, H, Hf, E, L, w,
-                  bf16, s);
+    const void* h1 = sv->h1;
+    const void* h3 = sv->h3;
+    if (recompute) {
+      // h1, h3 again from xd, straight into the dh1, dh3 buffers; the dA
+      // epilogue then reads each tile's h1, h3 before writing its dh1, dh3 at
+      // the same place (every element is read and written by one tile only)
+      launch_ffn_up(sv->xd, sv->cu_seqlens, sv->W1, sv->W3, b->dh1, b->dh3, nullptr, R, H, Hf, E, L,
+                    w, bf16, s);
+      h1 = b->dh1;
+      h3 = b->dh3;
+    }
+    launch_bwd_da(b->dy, sv->cu_seqlens, sv->W2, h1, h3, b->dh1, b->dh3, R, H, Hf, E, L, w, bf16, s);
   }
   // experts by descending row count (written by the tile table above)
   const int32_t* eorder = R > 0 ? reinterpret_cast<const int32_t*>(w + L.eorder) : nullptr;

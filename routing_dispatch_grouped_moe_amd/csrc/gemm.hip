@@ -103,9 +103,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
   if constexpr (EPI == EPI_STORE) {
     store1<BF16>(p.C0, o, v0);
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    store1<BF16>(p.C0, o, v0);
-    store1<BF16>(p.C1, o, v1);
-    store1<BF16>(p.C2, o, silu_f(v0) * v1);
+    // h1 (C0), h3 (C1) and a (C2); a null output is not written
+    if (p.C0) store1<BF16>(p.C0, o, v0);
+    if (p.C1) store1<BF16>(p.C1, o, v1);
+    if (p.C2) store1<BF16>(p.C2, o, silu_f(v0) * v1);
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     const float z = load1<BF16>(p.X0, o), u = load1<BF16>(p.X1, o);
     const float sg = sigmoid_f(z);
@@ -1076,18 +1077,21 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         put4(stage1, r, c, a);
       });
       __syncthreads();
-      store_rows(stage0, R256{}, p.C0, 0, R256{}, R0{});
-      store_rows(stage1, R256{}, p.C2, 0, R256{}, R0{});
-      __syncthreads();
-      StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
-        constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
-        const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        const float v1[4] = {acc[1][i][j][4 * g], acc[1][i][j][4 * g + 1], acc[1][i][j][4 * g + 2],
-                             acc[1][i][j][4 * g + 3]};
-        put4(stage0, r, c, v1);
-      });
-      __syncthreads();
-      store_rows(stage0, R256{}, p.C1, 0, R256{}, R0{});
+      // a null output (h1, h3 under recompute, or a when recomputing) is skipped
+      if (p.C0) store_rows(stage0, R256{}, p.C0, 0, R256{}, R0{});
+      if (p.C2) store_rows(stage1, R256{}, p.C2, 0, R256{}, R0{});
+      if (p.C1) {
+        __syncthreads();
+        StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
+          constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+          const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const float v1[4] = {acc[1][i][j][4 * g], acc[1][i][j][4 * g + 1], acc[1][i][j][4 * g + 2],
+                               acc[1][i][j][4 * g + 3]};
+          put4(stage0, r, c, v1);
+        });
+        __syncthreads();
+        store_rows(stage0, R256{}, p.C1, 0, R256{}, R0{});
+      }
     } else {
       // SwiGLU backward: four phases, one per 32-row group i of both
       // wavefront rows (64 tile rows).  A phase's h1 and h3 rows (32 KB each)

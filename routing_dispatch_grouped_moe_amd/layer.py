@@ -37,8 +37,10 @@ class MoELayer:
         self.row_of = e(R, dtype=i32)
         self.tok_of = e(R, dtype=i32)
         self.xd = e(R, H)
-        self.h1 = e(R, Hf)
-        self.h3 = e(R, Hf)
+        # under recompute h1, h3 are not kept between forward and backward
+        self.recompute = bool(flags & L.MOE_F_RECOMPUTE)
+        self.h1 = None if self.recompute else e(R, Hf)
+        self.h3 = None if self.recompute else e(R, Hf)
         self.a = e(R, Hf)
         self.y = e(R, H)
         self.out = e(S, H)

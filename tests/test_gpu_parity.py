@@ -51,7 +51,7 @@ def run_layer(wl, W1=None, W3=None, W2=None, bias=None, backward=True, flags=L.M
              "a", "y", "out"]
     if backward:
         names += ["dy", "dh1", "dh3", "dxd", "dgates", "dlogits", "dx", "dWg", "dW1", "dW3", "dW2"]
-    got = {n: to_host(getattr(layer, n)) for n in names}
+    got = {n: to_host(getattr(layer, n)) for n in names if getattr(layer, n) is not None}
     got["status"] = layer.status()
     return got
 
@@ -148,6 +148,32 @@ def test_layer_parity_raw_gates(cid, cfg, ov):
     assert np.count_nonzero(got["dlogits"]) > got["topk_idx"].size
     _say(f"[parity raw] {cid}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
          + f" flips={flips}")
+
+
+# Recompute instead of save: the forward keeps no h1/h3 and the backward
+# recomputes them into dh1/dh3 and runs the SwiGLU backward in place.  Same
+# kernels on the same inputs, so every output must equal the saving mode's
+# bit for bit (the saving mode is the one checked against the oracle above).
+RECOMPUTE_CASES = [
+    ("c1_fp32", "c1", {}),                                            # fp32 kernels
+    ("c2_w4", "c2", dict(S=300, H=256, Hf=384)),                      # 256-row tiles
+    ("c4_skewed", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),        # ragged, hot expert
+    ("c6_few_rows", "c6", dict(S=48, H=512, Hf=256)),                 # 64-row tiles
+]
+
+
+@pytest.mark.parametrize("cid,cfg,ov", RECOMPUTE_CASES, ids=[c[0] for c in RECOMPUTE_CASES])
+def test_recompute_matches_saving_mode_bitwise(cid, cfg, ov):
+    _say(f"[recompute] {cid}: {cfg} {ov}")
+    wl = make_workload(cfg, host_weights=True, **ov)
+    saved = run_layer(wl)
+    rec = run_layer(wl, flags=L.MOE_F_RENORM | L.MOE_F_RECOMPUTE)
+    assert rec["status"] == 0
+    assert "h1" not in rec and "h3" not in rec
+    for n, v in saved.items():
+        if n in ("h1", "h3", "status"):
+            continue
+        np.testing.assert_array_equal(rec[n], v, err_msg=f"{n} differs under recompute")
 
 
 @pytest.mark.parametrize("cfg,ov", [("c3", dict(S=257, H=256, Hf=256)),
