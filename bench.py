@@ -164,6 +164,8 @@ def main():
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
     ap.add_argument("--gates", default="renorm", choices=["renorm", "raw"],
                     help="gates renormalised over the K chosen experts (default) or raw softmax")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in one HIP graph (graph_ms_per_step)")
     ap.add_argument("--recompute", action="store_true",
                     help="keep no h1/h3 between forward and backward (the backward recomputes them)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -248,6 +250,28 @@ def main():
     ktab = L.moe_timer_read()
     L.moe_timer_reset()
 
+    graph_ms = None
+    if args.graph:
+        # the same step captured once in a HIP graph, replayed K times
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"timing {args.steps} graph replays")
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg0) / args.steps * 1e3
+        del g
+
     S_in = wl.S_in
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
@@ -308,6 +332,8 @@ def main():
                    else "raw softmax (no renormalisation)",
                    "activations": "h1, h3 recomputed in the backward" if args.recompute
                    else "h1, h3 saved"},
+        "graph_ms_per_step": graph_ms,
+        "graph_tokens_per_s": (S_in / (graph_ms / 1e3)) if graph_ms else None,
         "memory": {"layer_buffers_gb": held / 1e9, "kept_forward_to_backward_gb": kept / 1e9,
                    "peak_allocated_gb": torch.cuda.max_memory_allocated(dev) / 1e9},
         "roofline": roof,
