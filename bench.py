@@ -174,7 +174,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU expert-"
-              f"parallel path is not part of this build", file=sys.stderr)
+              f"parallel path is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

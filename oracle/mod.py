@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see oracle/moe.py for who may call it).
 Source: "PyTorch MoE/MoD Training Framework..." (ai-manual.ru), "Comparison
 with alternatives" (MoD: a share of the tokens skips the layer entirely, here
 50%) and "Who the framework saves" (the MoE+MoD combination).  The pages give
-no formula; the reading used (listed in the design doc):
+no formula; the reading used:
   * score r[s] = <x[s], w_r>, a raw linear score, rounded to float32;
   * per sequence keep the C tokens of largest score, ties to the lower
     position, listed in ascending position;

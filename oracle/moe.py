@@ -24,7 +24,7 @@ together ([FW] "What's in the box", sparse-backward item) and the weight
 gradients go to an fp32 buffer shaped like the weights ([MEP] guide, gradient
 buffer step).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * gates are renormalised over the K chosen experts (drop-in for the Mixtral
     block) unless ``renorm=False``;
   * the top-K order key is (logit descending, expert index ascending) on the
