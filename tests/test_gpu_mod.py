@@ -32,7 +32,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_and_check(wl, C=None, zero_scores=False):
+def run_and_check(wl, C=None, zero_scores=False, flags=L.MOE_F_RENORM):
     B, T = wl.cfg["B"], wl.cfg["T"]
     C = wl.cfg["C"] if C is None else C
     H, Hf, E, K = wl.H, wl.Hf, wl.E, wl.K
@@ -40,7 +40,8 @@ def run_and_check(wl, C=None, zero_scores=False):
     dev = lambda a: to_dev(a, "bf16")  # noqa: E731
     x, wr_t, Wg = dev(wl.x), dev(w_r), dev(wl.Wg)
     W1, W3, W2, dout = dev(wl.W1), dev(wl.W3), dev(wl.W2), dev(wl.dout)
-    layer = MoDMoELayer(B, T, C, H, Hf, E, K, "bf16")
+    layer = MoDMoELayer(B, T, C, H, Hf, E, K, "bf16", flags=flags)
+    renorm = bool(flags & L.MOE_F_RENORM)
     L.moe_clear_status(layer.moe.ws)
     layer.forward(x, wr_t, Wg, None, W1, W3, W2)
     layer.backward(dout, x, wr_t, Wg, W1, W3, W2)
@@ -57,7 +58,8 @@ def run_and_check(wl, C=None, zero_scores=False):
     logits = to_host(layer.moe.logits)
     idx = oracle.topk_experts(logits, K)
     np.testing.assert_array_equal(to_host(layer.moe.topk_idx), idx, err_msg="topk_idx")
-    fw = oracle.moe_forward(xk, wl.Wg, None, wl.W1, wl.W3, wl.W2, K, idx=idx, logits=logits)
+    fw = oracle.moe_forward(xk, wl.Wg, None, wl.W1, wl.W3, wl.W2, K, idx=idx, logits=logits,
+                            renorm=renorm)
     m = fw["out"]
     assert_close("m (MoE out)", to_host(layer.moe.out), m, BF16_TOL)
     out = oracle.mod_merge(wl.x, r, keep, m)
@@ -68,7 +70,7 @@ def run_and_check(wl, C=None, zero_scores=False):
                                   err_msg="dropped tokens must pass through unchanged")
 
     dm, dr, _, _ = oracle.mod_backward(wl.x, w_r, r, keep, m, wl.dout, None)
-    bw = oracle.moe_backward(fw, dm, xk, wl.Wg, wl.W1, wl.W3, wl.W2, K)
+    bw = oracle.moe_backward(fw, dm, xk, wl.Wg, wl.W1, wl.W3, wl.W2, K, renorm=renorm)
     _, _, dx, dw_r = oracle.mod_backward(wl.x, w_r, r, keep, m, wl.dout, bw["dx"])
     errs = {}
     errs["dm"] = assert_close("dm", to_host(layer.dm), dm, BF16_TOL)
@@ -108,3 +110,10 @@ def test_mod_zero_scores_keep_first_positions():
     # every score is 0: the tie rule keeps the first C positions of each sequence
     wl = make_workload("c5", S=256, H=128, Hf=128, E=4, host_weights=True)
     run_and_check(wl, zero_scores=True)
+
+
+def test_mod_raw_gates_and_recompute():
+    # the MoD block over a MoE layer with raw softmax gates that keeps no h1/h3
+    wl = make_workload("c5", S=512, H=256, Hf=384, host_weights=True)
+    errs = run_and_check(wl, flags=L.MOE_F_RECOMPUTE)
+    _say("[mod] raw gates + recompute " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
