@@ -96,7 +96,9 @@ typedef struct {
 } moe_dims_t;
 
 /* Bytes of workspace every call with these dims needs (the same for all
- * entry points).  Returns 0 for invalid dims.  Its first 4 bytes are the
+ * entry points; dims.flags included: raw softmax gates need more for the
+ * backward, so size with the flags the calls will carry).  Returns 0 for
+ * invalid dims.  Its first 4 bytes are the
  * device status word, which accumulates across calls until cleared with
  * moe_clear_status (clear it once for a new workspace); the rest needs no
  * initialisation. */

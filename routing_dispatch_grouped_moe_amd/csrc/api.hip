@@ -55,7 +55,7 @@ TimedLaunch::~TimedLaunch() {
 // ------------------------------------------------------------- workspace --
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
+WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t flags) {
   (void)Hf;
   WsLayout L{};
   const size_t esz = dtype == MOE_BF16 ? 2 : 4;
@@ -95,8 +95,10 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype) {
   L.route_part = off;
   off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
   L.route_tickets = off; off = align256(off + (size_t)std::max(L.route_groups, 1) * 4);
+  // raw softmax gates only: token-slice partials of the dense dWg
   L.dwg_dense_part = off;
-  off = align256(off + (size_t)dwg_dense_splits(S, H, L.epad) * H * L.epad * 4);
+  if (!(flags & MOE_F_RENORM))
+    off = align256(off + (size_t)dwg_dense_splits(S, H, L.epad) * H * L.epad * 4);
   L.total = off;
   return L;
 }
@@ -131,7 +133,7 @@ static moe_status_t check_ptrs(std::initializer_list<const void*> ps) {
 static moe_status_t check_ws(const moe_dims_t* d, const void* ws, size_t ws_bytes) {
   if (!ws) return MOE_ERR_NULL;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
-  if (ws_bytes < ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype).total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags).total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -149,7 +151,7 @@ extern "C" {
 
 size_t moe_workspace_bytes(const moe_dims_t* d) {
   if (check_dims(d) != MOE_OK) return 0;
-  return ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype).total;
+  return ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags).total;
 }
 
 const char* moe_status_string(moe_status_t st) {
@@ -193,7 +195,7 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   MOE_TRY(check_ptrs({x, Wg, topk_idx, gates, counts}));
   if ((bias && !aligned16(bias)) || (logits && !aligned16(logits))) return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;
@@ -224,7 +226,7 @@ moe_status_t moe_dispatch(const moe_dims_t* d, const void* x, const int32_t* top
   if (d->S == 0) MOE_TRY(check_ptrs({cu_seqlens}));  // only cu_seqlens (all zeros) is written
   else MOE_TRY(check_ptrs({x, topk_idx, cu_seqlens, row_of, tok_of, xd}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   launch_dispatch(x, topk_idx, cu_seqlens, row_of, tok_of, xd, L, reinterpret_cast<char*>(ws),
                   d->S, d->H, d->E, d->K, d->dtype == MOE_BF16,
                   reinterpret_cast<hipStream_t>(stream));
@@ -240,7 +242,7 @@ moe_status_t moe_ffn_up(const moe_dims_t* d, const void* xd, const int32_t* cu, 
   MOE_TRY(check_ptrs({xd, cu, W1, W3, a}));
   if (keep_h) MOE_TRY(check_ptrs({h1, h3}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const int64_t R = d->S * d->K;
@@ -258,7 +260,7 @@ moe_status_t moe_ffn_down(const moe_dims_t* d, const void* a, const int32_t* cu,
   if (d->S == 0) return MOE_OK;
   MOE_TRY(check_ptrs({a, cu, W2, y}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const int64_t R = d->S * d->K;
@@ -278,7 +280,7 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* d, const void* xd, const int32_t*
   MOE_TRY(check_ptrs({xd, cu, W1, W3, W2, a, y}));
   if (keep_h) MOE_TRY(check_ptrs({h1, h3}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;
@@ -311,7 +313,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
   if (d->S == 0) {  // no tokens: the weight gradients are zero (or unchanged when accumulating)
     MOE_TRY(check_ptrs({sv->cu_seqlens, dWg, dW1, dW3, dW2}));
     MOE_TRY(check_ws(d, ws, ws_bytes));
-    const WsLayout L = ws_layout(0, d->H, d->Hf, d->E, d->K, d->dtype);
+    const WsLayout L = ws_layout(0, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = d->dtype == MOE_BF16, accum = (d->flags & MOE_F_ACCUM_GRAD) != 0;
     launch_bwd_dw2(nullptr, nullptr, sv->cu_seqlens, nullptr, dW2, 0, d->H, d->Hf, d->E, accum,
@@ -330,7 +332,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                       b->dlogits}));
   if (raw) MOE_TRY(check_ptrs({sv->logits}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
-  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype);
+  const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;

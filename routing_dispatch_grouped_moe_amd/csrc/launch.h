@@ -47,7 +47,8 @@ struct WsLayout {
   int route_groups;   // 32-token groups of the router
   int route_parts;    // K parts per group (1: no split)
 };
-WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype);
+// the layout depends on the flags: raw softmax gates add the dense dWg partials
+WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t flags);
 
 constexpr int kGemmBM = 256;   // M tile of the grouped GEMMs (rows per tile)
 constexpr int kGemmBMFew = 64; // M tile when experts average at most kFewRows rows (bf16)
