@@ -638,23 +638,24 @@ void launch_dx_dense(const void* dxd, const int32_t* row_of, const float* dlogit
   else with_kt<DxDenseLaunch, false>(K, dxd, row_of, dlogits, wgT, dx, S, H, E, K, R, s);
 }
 
-// dWg partials: block (256 columns h, 16 experts, token slice z); thread
-// (ty, tx) holds experts 2 ty, 2 ty + 1 of columns 8 tx .. 8 tx + 7, summing
-// the slice's tokens in order; part[z][h][e] (e over epad).
+// dWg partials: block (256 columns h, 32 experts, token slice z); thread
+// (ty, tx) holds experts 4 ty .. 4 ty + 3 of columns 8 tx .. 8 tx + 7 (32 fp32
+// FMAs per three LDS reads), summing the slice's tokens in order;
+// part[z][h][e] (e over epad).
 template <bool BF16>
 __global__ __launch_bounds__(256) void dwg_dense_kernel(const void* __restrict__ x,
                                                         const float* __restrict__ dlogits,
                                                         float* __restrict__ part, int S, int H,
                                                         int E, int epad, int per_split) {
-  constexpr int TS = 32, TH = 256, TE = 16;
+  constexpr int TS = 32, TH = 256, TE = 32;
   __shared__ __attribute__((aligned(16))) float sx[TS][TH];
-  __shared__ float sd[TS][TE];
+  __shared__ __attribute__((aligned(16))) float sd[TS][TE];
   const int h0 = blockIdx.x * TH, e0 = blockIdx.y * TE, z = blockIdx.z;
   const int s_lo = z * per_split, s_hi = min(S, s_lo + per_split);
   const int tid = threadIdx.x, tx = tid & 31, ty = tid >> 5;
-  float acc[2][8];
+  float acc[4][8];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
   for (int t0 = s_lo; t0 < s_hi; t0 += TS) {
@@ -674,23 +675,25 @@ __global__ __launch_bounds__(256) void dwg_dense_kernel(const void* __restrict__
     for (int t = 0; t < TS; ++t) {
       const float4 w0 = *reinterpret_cast<const float4*>(&sx[t][8 * tx]);
       const float4 w1 = *reinterpret_cast<const float4*>(&sx[t][8 * tx + 4]);
+      const float4 dq = *reinterpret_cast<const float4*>(&sd[t][4 * ty]);
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      const float d0 = sd[t][2 * ty], d1 = sd[t][2 * ty + 1];
+      const float d[4] = {dq.x, dq.y, dq.z, dq.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[0][i] = fmaf(d0, w[i], acc[0][i]);
-        acc[1][i] = fmaf(d1, w[i], acc[1][i]);
-      }
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[q][i] = fmaf(d[q], w[i], acc[q][i]);
     }
     __syncthreads();
   }
   const int h = h0 + 8 * tx;
   if (h >= H) return;
-  float* o = part + ((size_t)z * H + h) * epad + e0 + 2 * ty;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    o[(size_t)i * epad] = acc[0][i];
-    o[(size_t)i * epad + 1] = acc[1][i];
+  for (int q = 0; q < 4; ++q) {
+    const int e = e0 + 4 * ty + q;
+    if (e >= epad) continue;
+    float* o = part + ((size_t)z * H + h) * epad + e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[(size_t)i * epad] = acc[q][i];
   }
 }
 
@@ -707,9 +710,11 @@ __global__ __launch_bounds__(256) void dwg_dense_reduce_kernel(const float* __re
   dWg[i] = accum ? dWg[i] + v : v;
 }
 
+// token slices of the dense dWg: about 1024 blocks in all (several waves,
+// so the last one is short), at least 32 tokens per slice, at most 64 slices
 int dwg_dense_splits(int64_t S, int H, int epad) {
-  const int64_t blocks = (int64_t)((H + 255) / 256) * (epad / 16);
-  int64_t n = blocks >= 256 ? 1 : 256 / blocks;
+  const int64_t blocks = (int64_t)((H + 255) / 256) * ((epad + 31) / 32);
+  int64_t n = (1024 + blocks - 1) / blocks;
   const int64_t chunks = (S + 31) / 32;
   if (n > chunks) n = chunks;
   return (int)(n < 1 ? 1 : (n > 64 ? 64 : n));
@@ -722,7 +727,7 @@ void launch_dwg_dense(const void* x, const float* dlogits, float* dWg, const WsL
   const int per = (int)(((S + ns - 1) / ns + 31) / 32 * 32);
   {
     TimedLaunch tl("router_dWg_partial", s);
-    dim3 grid((H + 255) / 256, L.epad / 16, ns);
+    dim3 grid((H + 255) / 256, (L.epad + 31) / 32, ns);
     if (bf16)
       hipLaunchKernelGGL(dwg_dense_kernel<true>, grid, dim3(256), 0, s, x, dlogits, part, (int)S, H,
                          E, L.epad, per);
