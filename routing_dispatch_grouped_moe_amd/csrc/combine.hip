@@ -550,9 +550,10 @@ void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* d
 // Both are fp32 FMA tiles through LDS (E is small next to H: the products
 // are 2 S H E flops, a few percent of the expert GEMMs).
 
-// Block: 32 tokens x 256 columns; thread (ty, tx) holds tokens 4 ty .. 4 ty + 3
-// and columns 8 tx .. 8 tx + 7; experts in chunks of 16 through LDS (dl as
-// [e][token], the row-major transposed router weight as [e][column]).
+// Block: 64 tokens x 256 columns; thread (ty, tx) holds tokens 8 ty .. 8 ty + 7
+// and columns 8 tx .. 8 tx + 7 (64 fp32 FMAs per four LDS reads); experts in
+// chunks of 16 through LDS (dl as [e][token], the row-major transposed router
+// weight as [e][column]).
 template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void dx_dense_kernel(const void* __restrict__ dxd,
                                                        const int32_t* __restrict__ row_of,
@@ -560,14 +561,14 @@ __global__ __launch_bounds__(256) void dx_dense_kernel(const void* __restrict__ 
                                                        const void* __restrict__ wgT,
                                                        void* __restrict__ dx, int S, int H, int E,
                                                        int K, int64_t R) {
-  constexpr int TS = 32, TH = 256, TE = 16;
-  __shared__ float sd[TE][TS + 1];
+  constexpr int TS = 64, TH = 256, TE = 16;
+  __shared__ __attribute__((aligned(16))) float sd[TE][TS];
   __shared__ __attribute__((aligned(16))) float sw[TE][TH];
   const int s0 = blockIdx.x * TS, h0 = blockIdx.y * TH;
   const int tid = threadIdx.x, tx = tid & 31, ty = tid >> 5;
-  float acc[4][8];
+  float acc[8][8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
   for (int e0 = 0; e0 < E; e0 += TE) {
@@ -583,25 +584,26 @@ __global__ __launch_bounds__(256) void dx_dense_kernel(const void* __restrict__ 
       *reinterpret_cast<float4*>(&sw[e][c + 4]) = make_float4(v[4], v[5], v[6], v[7]);
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
     for (int e = 0; e < TE; ++e) {
       const float4 w0 = *reinterpret_cast<const float4*>(&sw[e][8 * tx]);
       const float4 w1 = *reinterpret_cast<const float4*>(&sw[e][8 * tx + 4]);
+      const float4 d0 = *reinterpret_cast<const float4*>(&sd[e][8 * ty]);
+      const float4 d1 = *reinterpret_cast<const float4*>(&sd[e][8 * ty + 4]);
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float d = sd[e][4 * ty + j];
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(d, w[i], acc[j][i]);
-      }
+        for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(d[j], w[i], acc[j][i]);
     }
     __syncthreads();
   }
   const int h = h0 + 8 * tx;
   if (h >= H) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = s0 + 4 * ty + j;
+  for (int j = 0; j < 8; ++j) {
+    const int t = s0 + 8 * ty + j;
     if (t >= S) continue;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -624,7 +626,7 @@ template <bool BF16, int KT>
 struct DxDenseLaunch {
   static void run(const void* dxd, const int32_t* row_of, const float* dlogits, const void* wgT,
                   void* dx, int64_t S, int H, int E, int K, int64_t R, hipStream_t s) {
-    hipLaunchKernelGGL((dx_dense_kernel<BF16, KT>), dim3((unsigned)((S + 31) / 32), (H + 255) / 256),
+    hipLaunchKernelGGL((dx_dense_kernel<BF16, KT>), dim3((unsigned)((S + 63) / 64), (H + 255) / 256),
                        dim3(256), 0, s, dxd, row_of, dlogits, wgT, dx, (int)S, H, E, K, R);
   }
 };
