@@ -276,8 +276,10 @@ def main():
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
     counts = moe.counts.cpu().numpy().tolist()
-    c = np.asarray(counts, np.float64)
-    maxvio = float(c.max() / c.mean() - 1.0)
+    # load statistics of the routing histogram, from the library
+    stats = torch.empty(2, dtype=torch.float32, device=dev)
+    L.moe_load_stats(wl.E, moe.counts, stats)
+    maxvio, load_entropy = (float(v) for v in stats.cpu().numpy())
     mcfg = dict(S=moe.S, H=wl.H, Hf=wl.Hf, E=wl.E, K=wl.K, dtype=wl.dtype,
                 raw=args.gates == "raw")
 
@@ -326,7 +328,8 @@ def main():
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg["workload"], "tokens": S_in, "moe_tokens": moe.S, "H": wl.H,
                    "H_ffn": wl.Hf, "experts": wl.E, "top_k": wl.K, "router_bias_beta": wl.beta,
-                   "maxvio_measured": maxvio, "parallelism": "single GPU, all experts resident",
+                   "maxvio_measured": maxvio, "load_entropy": load_entropy,
+                   "parallelism": "single GPU, all experts resident",
                    "step": "forward" if fwd_only else "forward+backward",
                    "gates": "softmax renormalised over the top-K" if args.gates == "renorm"
                    else "raw softmax (no renormalisation)",
