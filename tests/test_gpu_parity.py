@@ -132,6 +132,8 @@ RAW_CASES = [
     ("c2_mixtral_shape_raw", "c2", dict(S=300, H=256, Hf=384)),
     ("c3_zipf_raw", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_skewed_raw", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
+    # K = E: the raw gates are the whole softmax (they sum to one)
+    ("c2_raw_every_expert", "c2", dict(S=130, H=128, Hf=256, E=4, K=4)),
 ]
 
 
@@ -143,9 +145,13 @@ def test_layer_parity_raw_gates(cid, cfg, ov):
     assert got["status"] == 0
     tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
     errs, flips = check_against_oracle(wl, got, tol, renorm=False)
-    # raw gates do not sum to one; dlogits is non-zero off the chosen experts
-    assert np.all(got["gates"].sum(axis=1) < 1.0 + 1e-6)
-    assert np.count_nonzero(got["dlogits"]) > got["topk_idx"].size
+    gsum = got["gates"].sum(axis=1)
+    if wl.K == wl.E:
+        np.testing.assert_allclose(gsum, 1.0, atol=1e-5)
+    else:
+        # raw gates do not sum to one; dlogits is non-zero off the chosen experts
+        assert np.all(gsum < 1.0 + 1e-6)
+        assert np.count_nonzero(got["dlogits"]) > got["topk_idx"].size
     _say(f"[parity raw] {cid}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
          + f" flips={flips}")
 
