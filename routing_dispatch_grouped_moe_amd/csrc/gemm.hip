@@ -1093,60 +1093,46 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         store_rows(stage0, R256{}, p.C1, 0, R256{}, R0{});
       }
     } else {
-      // SwiGLU backward: four phases, one per 32-row group i of both
-      // wavefront rows (64 tile rows).  A phase's h1 and h3 rows (32 KB each)
-      // come into one stage with coalesced loads while the previous phase is
-      // computed from the other; dh1 and dh3 overwrite them in place and
-      // leave as whole rows.
+      // SwiGLU backward: two phases of 128 tile rows (row blocks 2ph and
+      // 2ph + 1 of both wavefront rows).  A phase's h1 rows come into stage 0
+      // and its h3 rows into stage 1 by direct loads (no staging registers),
+      // dh1 and dh3 overwrite them in place and leave as whole rows.
       static_assert(EPI == EPI_SWIGLU_BWD && NB == 1 && BM == 256 && BN == 256, "dA epilogue tile");
-      constexpr int kHalfB = 64 * RS;                  // one matrix of a phase in a stage
-      constexpr int kLd = 2 * 64 * LPR / kThreads4;    // 16-byte loads per lane per phase
-      const uint16_t* h1 = reinterpret_cast<const uint16_t*>(p.X0);
-      const uint16_t* h3 = reinterpret_cast<const uint16_t*>(p.X1);
-      // staged row q of a phase holds tile row (q / 32) * 128 + 32 i + q % 32.
-      // 16-byte piece u * kThreads4 + tid of a phase: matrix u / (kLd / 2),
-      // staged row q0 + kStep (u % (kLd / 2)), chunk tid % LPR.
-      constexpr int kStep = kThreads4 / LPR;
-      static_assert(kThreads4 % LPR == 0 && (kLd / 2) * kStep == 64 && 32 % kStep == 0, "phase pieces");
-      const int q0 = tid / LPR;
-      const int64_t cofs = min(n0 + 8 * (tid % LPR), p.N - 8);
-      const uint16_t* z1 = h1 + row0 * p.ldc + cofs;   // row 0 of the tile
-      const uint16_t* z3 = h3 + row0 * p.ldc + cofs;
-      const int64_t oq0 = (int64_t)q0 * p.ldc;
-      u32x4 pre[kLd];
-      auto load_phase = [&](int i) {
+      static_assert(MI == 4 && RS == 512, "two 128-row phases of 256 columns");
+      // staged row q of phase ph is tile row 64 ph + q (q < 64) or
+      // 128 + 64 ph + (q - 64); wavefront w loads 32 KB of one matrix:
+      // instruction u covers staged rows 2 (32 (w & 1) + u) and the next one
+      const int mat = w >> 1, hl = lane >> 5, slot = lane & 31;
+      const char* xbase = reinterpret_cast<const char*>(mat ? p.X1 : p.X0) +
+                          ((int64_t)row0 * p.ldc + n0) * 2;
+      char* dstage = mat ? stage1 : stage0;
+      auto dma_phase = [&](int ph) {
+        // rows past the tile's valid ones and columns past N read zeros
+        const int64_t rows_left = (int64_t)valid - 64 * ph;
+        const int64_t lim = rows_left > 0 ? ((rows_left - 1) * p.ldc + (p.N - n0)) * 2 : 0;
+        const u32x4 rs = rsrc_words(xbase + (int64_t)64 * ph * p.ldc * 2, (uint32_t)lim);
 #pragma unroll
-        for (int u = 0; u < kLd; ++u) {
-          const int qd = kStep * (u % (kLd / 2));
-          const int rd = 32 * i + qd + (qd / 32) * 96;   // tile row minus q0
-          // rows past the tile's valid ones read row 0 (never stored)
-          const uint16_t* z = u < kLd / 2 ? z1 : z3;
-          const uint16_t* src = rd + q0 < valid ? z + oq0 + (int64_t)rd * p.ldc : z;
-          pre[u] = *reinterpret_cast<const u32x4*>(src);
+        for (int u = 0; u < 32; ++u) {
+          const int j = 32 * (w & 1) + u, q = 2 * j + hl;
+          const int r = q < 64 ? q : q + 64;  // tile row minus 64 ph
+          const uint32_t voff = ((uint32_t)r * (uint32_t)p.ldc + 8u * (uint32_t)(slot ^ (q & 15))) * 2u;
+          dma16(rs, voff, dstage + j * 1024);
         }
       };
-      auto put_phase = [&](char* st) {
-#pragma unroll
-        for (int u = 0; u < kLd; ++u) {
-          const int f = u * kThreads4 + tid;
-          const int m = f / (64 * LPR), q = (f / LPR) % 64, c = f % LPR;
-          *reinterpret_cast<u32x4*>(st + m * kHalfB + (uint32_t)q * RS + ((uint32_t)(c ^ (q & 15)) << 4)) = pre[u];
-        }
-      };
-      load_phase(0);
-      put_phase(stage0);
-      StaticFor<0, MI>::run([&](auto i_tag) {
-        constexpr int i = decltype(i_tag)::value;
-        char* st = (i & 1) ? stage1 : stage0;
-        if constexpr (i + 1 < MI) load_phase(i + 1);
-        __syncthreads();
-        const int q = wm * 32 + (lane & 31);
-        StaticFor<0, NJ * 4>::run([&](auto jg_tag) {
-          constexpr int jg = decltype(jg_tag)::value, j = jg / 4, g = jg % 4;
+      dma_phase(0);
+      StaticFor<0, 2>::run([&](auto ph_tag) {
+        constexpr int ph = decltype(ph_tag)::value;
+        // this wavefront's loads (and, from the second phase on, its stores
+        // of the previous one) are done; after the barrier everyone's are
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        StaticFor<0, 2 * NJ * 4>::run([&](auto x_tag) {
+          constexpr int x = decltype(x_tag)::value, ib = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
+          constexpr int i = 2 * ph + ib;
+          const int q = wm * 64 + ib * 32 + (lane & 31);
           const int c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
           float z[4], u[4], d1[4], d3[4];
-          get4(st, q, c, z);
-          get4(st + kHalfB, q, c, u);
+          get4(stage0, q, c, z);
+          get4(stage1, q, c, u);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const float v = acc[0][i][j][4 * g + t];
@@ -1155,13 +1141,17 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
             d3[t] = vs * z[t];
             d1[t] = vs * u[t] * (1.0f + z[t] - z[t] * sg);
           }
-          put4(st, q, c, d1);
-          put4(st + kHalfB, q, c, d3);
+          put4(stage0, q, c, d1);
+          put4(stage1, q, c, d3);
         });
         __syncthreads();
-        store_rows(st, R64{}, p.C0, 32 * i, R32{}, R96{});
-        store_rows(st + kHalfB, R64{}, p.C1, 32 * i, R32{}, R96{});
-        if constexpr (i + 1 < MI) put_phase((i & 1) ? stage0 : stage1);
+        store_rows(stage0, R128{}, p.C0, 64 * ph, R64{}, R64{});
+        store_rows(stage1, R128{}, p.C1, 64 * ph, R64{}, R64{});
+        if constexpr (ph == 0) {
+          // every wavefront has read the stages for its stores
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          dma_phase(1);
+        }
       });
     }
   } else {
