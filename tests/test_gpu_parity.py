@@ -264,11 +264,12 @@ def test_zero_tokens():
     assert not to_host(layer.dW1).any() and not to_host(layer.dWg).any()
 
 
-@pytest.mark.parametrize("cid,cfg,ov", [
-    ("c3_zipf_small_accum", "c3", dict(S=257, H=256, Hf=256)),
-    ("c2_multi_tile_accum", "c2", dict(S=2100, H=256, Hf=384, E=12)),
-], ids=["c3_zipf_small_accum", "c2_multi_tile_accum"])
-def test_accumulated_weight_gradients(cid, cfg, ov):
+@pytest.mark.parametrize("cid,cfg,ov,flags", [
+    ("c3_zipf_small_accum", "c3", dict(S=257, H=256, Hf=256), L.MOE_F_RENORM),
+    ("c2_multi_tile_accum", "c2", dict(S=2100, H=256, Hf=384, E=12), L.MOE_F_RENORM),
+    ("c2_raw_gates_recompute_accum", "c2", dict(S=300, H=256, Hf=384), L.MOE_F_RECOMPUTE),
+], ids=["c3_zipf_small_accum", "c2_multi_tile_accum", "c2_raw_gates_recompute_accum"])
+def test_accumulated_weight_gradients(cid, cfg, ov, flags):
     """MOE_F_ACCUM_GRAD adds the step's weight gradients to what the buffers hold.
 
     The buffers are prefilled with a known pattern P; afterwards dW - P must
@@ -285,7 +286,7 @@ def test_accumulated_weight_gradients(cid, cfg, ov):
     x, Wg = to_dev(wl.x, dt), to_dev(wl.Wg, dt)
     W1, W3, W2, dout = to_dev(wl.W1, dt), to_dev(wl.W3, dt), to_dev(wl.W2, dt), to_dev(wl.dout, dt)
     b = torch.from_numpy(bias).cuda()
-    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt, flags=L.MOE_F_RENORM | L.MOE_F_ACCUM_GRAD)
+    layer = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt, flags=flags | L.MOE_F_ACCUM_GRAD)
     pats = {}
     for n in ("dW1", "dW3", "dW2", "dWg"):
         g = getattr(layer, n)
@@ -299,7 +300,8 @@ def test_accumulated_weight_gradients(cid, cfg, ov):
     counts = to_host(layer.counts)
     assert counts[wl.E - 1] == 0
     _, bw = oracle_on_gpu_routing(wl.x, wl.Wg, bias, wl.W1, wl.W3, wl.W2, wl.K,
-                                  to_host(layer.logits), wl.dout)
+                                  to_host(layer.logits), wl.dout,
+                                  renorm=bool(flags & L.MOE_F_RENORM))
     for n in ("dW1", "dW3", "dW2", "dWg"):
         got = to_host(getattr(layer, n)).astype(np.float64) - pats[n]
         assert_close(f"{n} increment", got, bw[n], BF16_TOL)
