@@ -543,8 +543,10 @@ void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* d
 }
 
 // ------------------------------------------- router backward, raw softmax --
-// With raw softmax gates every expert's logit has a gradient, so the router
-// terms are dense products over all E experts:
+// Raw softmax gates (the MoE/MoD framework page's routing/gating item read
+// literally: a softmax over the experts, the chosen probabilities used as
+// gates without renormalisation).  Every expert's logit then has a gradient,
+// so the router terms are dense products over all E experts:
 //   dx[s]  = sum_k dxd[row_of[s*K+k]] + sum_e dl[s,e] Wg[:, e]
 //   dWg    = x^T dl
 // Both are fp32 FMA tiles through LDS (E is small next to H: the products

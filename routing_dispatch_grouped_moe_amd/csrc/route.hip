@@ -512,9 +512,10 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
 #undef ROUTE_CASE
 }
 
-// Load statistics of the routing histogram: one block of 1024 threads, one
-// expert each; the sums and the maximum meet through the wavefront
-// reductions and LDS in a fixed order (deterministic).
+// Load statistics of the routing histogram (the MoonEP page's load measure
+// maxvio = max load / mean load - 1, and the entropy of the load shares):
+// one block of 1024 threads, one expert each; the sums and the maximum meet
+// through the wavefront reductions and LDS in a fixed order (deterministic).
 __global__ __launch_bounds__(1024) void load_stats_kernel(const int32_t* __restrict__ counts,
                                                           int E, float* __restrict__ stats) {
   __shared__ float part[3][16];
