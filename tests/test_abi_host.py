@@ -4,6 +4,8 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -128,3 +130,53 @@ def test_status_strings(L):
     lib = _raw(L)
     for code, name in [(0, b"ok"), (5, b"workspace too small"), (7, b"HIP launch error")]:
         assert lib.moe_status_string(code) == name
+
+
+def _expected_dims_status(S, H, Hf, E, K, dtype):
+    """The size contract stated in include/moe.h, restated: 0 for valid dims, else the error."""
+    if dtype not in (0, 1):
+        return 3
+    if S < 0 or H <= 0 or Hf <= 0 or E <= 0 or K <= 0:
+        return 2
+    if E > 1024 or K > 16 or K > E:
+        return 6
+    if H % 128 or Hf % 128 or H > 65536 or Hf > 65536:
+        return 6
+    if S * K >= 2 ** 31 or S * max(H, Hf) >= 2 ** 30 or H * Hf >= 2 ** 30:
+        return 2
+    return 0
+
+
+def test_dims_contract_on_random_sizes(L):
+    """Random sizes around every limit: the library accepts exactly the documented ones.
+
+    Valid dims size a workspace (> 0, 256-aligned); invalid dims size none and
+    make every entry point return the documented error before anything is
+    launched.  Valid dims are only ever passed with NULL tensors, so the calls
+    stop at argument validation (MOE_ERR_NULL) and never reach a kernel.
+    """
+    lib = _raw(L)
+    rng = np.random.default_rng(11)
+    picks = {
+        "S": [0, 1, 63, 8192, 2 ** 20, 2 ** 27, -1],
+        "H": [128, 256, 4096, 7168, 65536, 65536 + 128, 100, 0, -128],
+        "Hf": [128, 1408, 2048, 14336, 65536, 131072, 200, 0],
+        "E": [1, 8, 384, 1024, 1025, 0, -3],
+        "K": [1, 2, 8, 16, 17, 0],
+        "dtype": [0, 1, 2, -1],
+    }
+    for _ in range(400):
+        v = {k: int(rng.choice(c)) for k, c in picks.items()}
+        want = _expected_dims_status(**v)
+        d = L.Dims(v["S"], v["H"], v["Hf"], v["E"], v["K"], v["dtype"], 1)
+        nb = lib.moe_workspace_bytes(C.byref(d))
+        if want == 0:
+            assert nb > 0 and nb % 256 == 0, v
+            st = lib.moe_route(C.byref(d), None, None, None, None, None, None, None, None, 0, None)
+            assert st == 1, (v, st)
+        else:
+            assert nb == 0, v
+            st = lib.moe_route(C.byref(d), None, None, None, None, None, None, None, None, 0, None)
+            assert st == want, (v, st, want)
+            st = lib.moe_combine(C.byref(d), None, None, None, None, None)
+            assert st == want, (v, st, want)
