@@ -108,6 +108,12 @@ CASES = [
     # 64-row tiles with a hot expert spanning several of them (ragged tail):
     # 400 rows over 16 experts, the Zipf-biased top expert takes most tokens
     ("c4_few_rows_hot_expert", "c4", dict(S=200, H=256, Hf=384, E=16, K=2, beta=4.0)),
+    # the largest expert count and top-K the library accepts (1024 experts,
+    # top-16; 2080 rows): spread over ~850 experts of at most ten rows each,
+    # and Zipf-concentrated on ~28 experts with every token in the hottest
+    # ones (several 64-row tiles each) and ~1000 experts empty
+    ("max_experts_top16_spread", "c4", dict(S=130, H=128, Hf=128, E=1024, K=16, beta=0.0)),
+    ("max_experts_top16_zipf", "c3", dict(S=130, H=128, Hf=128, E=1024, K=16)),
 ]
 
 
@@ -134,6 +140,8 @@ RAW_CASES = [
     ("c4_moonep_skewed_raw", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
     # K = E: the raw gates are the whole softmax (they sum to one)
     ("c2_raw_every_expert", "c2", dict(S=130, H=128, Hf=256, E=4, K=4)),
+    # dense logit gradient over the largest expert count, top-16
+    ("max_experts_top16_raw", "c4", dict(S=130, H=128, Hf=128, E=1024, K=16, beta=0.0)),
 ]
 
 
