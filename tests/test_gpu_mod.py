@@ -90,6 +90,11 @@ CASES = [
     ("mod_T128", 512, dict(H=256, Hf=384)),
     ("mod_T100_ragged", 400, dict(H=256, Hf=256)),
     ("mod_T37_odd", 148, dict(H=128, Hf=256, E=8)),
+    # the longest sequence the selection accepts (T = 8192: the sort fills
+    # its whole LDS key array), and T = 5000, which pads 3192 zero keys to
+    # the next power of two
+    ("mod_T8192_longest", 32768, dict(H=128, Hf=128)),
+    ("mod_T5000_padded_sort", 20000, dict(H=128, Hf=128)),
 ]
 
 
