@@ -1217,14 +1217,17 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
 
 // ---------------------------------------------------------- fp32 kernel --
 // M tile of kGemmBM rows x 32 columns; thread (tid % 32) owns a column,
-// rows tid/32 + 8 i.
-constexpr int kBMf = kGemmBM, kBNf = 32;
+// rows tid/32 + 8 i.  The K-grouped products (weight gradients) take 64-row
+// tiles: their grid is E x (M / 64) x (N / 32), four times the blocks of
+// 256-row tiles for the same work.
+constexpr int kBMf = kGemmBM, kBNf = 32, kBMfK = 64;
 
 template <bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int kBM = KGROUP ? kBMfK : kBMf;
   int e, valid, m0, n0;
   int64_t row0;
-  if (!tile_of<KGROUP, kBMf, kBNf>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+  if (!tile_of<KGROUP, kBM, kBNf>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
   const int tid = threadIdx.x;
   const int col = n0 + (tid & 31);
   if (col >= p.N) return;
@@ -1232,31 +1235,78 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const float* A1 = reinterpret_cast<const float*>(p.A1);
   const float* B0 = reinterpret_cast<const float*>(p.B0);
   const float* B1 = reinterpret_cast<const float*>(p.B1);
-  for (int i = 0; i < kBMf / 8; ++i) {
-    const int r = (tid >> 5) + 8 * i;
-    float acc0 = 0.f, acc1 = 0.f;
-    if constexpr (KGROUP) {
-      if (m0 + r >= p.M) continue;
-      // C_e[m0+r, col] = sum over the expert's rows k of A[k, m0+r] * B[k, col]
+  // Every output is one fmaf chain in ascending k.  The loads do not depend
+  // on the chain, so they are issued ahead of it: four k per 16-byte load
+  // along a contiguous K (K, lda, ldb multiples of 128, pointers 16-byte
+  // aligned), and in the K-grouped form four output rows per pass.
+  if constexpr (KGROUP) {
+    constexpr int kRows = 4;
+    for (int i0 = 0; i0 < kBM / 8; i0 += kRows) {
+      int rr[kRows];
+      float acc0[kRows], acc1[kRows];
+#pragma unroll
+      for (int j = 0; j < kRows; ++j) {
+        rr[j] = m0 + (tid >> 5) + 8 * (i0 + j);
+        acc0[j] = acc1[j] = 0.f;
+      }
+      if (rr[0] >= p.M) break;  // rows ascend with i0 and j
+      // C_e[rr, col] = sum over the expert's rows k of A[k, rr] * B[k, col];
+      // rows past M read row M - 1 and are not stored
       for (int k = 0; k < valid; ++k) {
         const int64_t gr = row0 + k;
-        const float a = A0[gr * p.lda + m0 + r];
-        acc0 = fmaf(a, B0[gr * p.ldb + col], acc0);
-        if constexpr (DUAL) acc1 = fmaf(a, B1[gr * p.ldb + col], acc1);
+        const float b0 = B0[gr * p.ldb + col];
+        const float b1 = DUAL ? B1[gr * p.ldb + col] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+          const float a = A0[gr * p.lda + min(rr[j], p.M - 1)];
+          acc0[j] = fmaf(a, b0, acc0[j]);
+          if constexpr (DUAL) acc1[j] = fmaf(a, b1, acc1[j]);
+        }
       }
-      if (valid > 0 || EPI != EPI_F32_ACC) epilogue<EPI, false, DUAL>(p, e, m0 + r, col, acc0, acc1);
-    } else {
-      if (r >= valid) continue;
+#pragma unroll
+      for (int j = 0; j < kRows; ++j)
+        if (rr[j] < p.M && (valid > 0 || EPI != EPI_F32_ACC))
+          epilogue<EPI, false, DUAL>(p, e, rr[j], col, acc0[j], acc1[j]);
+    }
+  } else {
+    static_assert(!(DUAL && B_KC), "the dual product reads row-major weights");
+    for (int i = 0; i < kBM / 8; ++i) {
+      const int r = (tid >> 5) + 8 * i;
+      if (r >= valid) break;  // rows ascend with i
       const int64_t gr = row0 + r;
+      float acc0 = 0.f, acc1 = 0.f;
       for (int seg = 0; seg < (TWOSEG ? 2 : 1); ++seg) {
-        const float* A = seg ? A1 : A0;
+        const float* arow = (seg ? A1 : A0) + gr * p.lda;
         const float* Bw = (seg ? B1 : B0) + (int64_t)e * p.sBe;
         const float* Bw1 = B1 + (int64_t)e * p.sBe;
-        for (int k = 0; k < p.K; ++k) {
-          const float a = A[gr * p.lda + k];
-          const float b0 = B_KC ? Bw[(int64_t)col * p.ldb + k] : Bw[(int64_t)k * p.ldb + col];
-          acc0 = fmaf(a, b0, acc0);
-          if constexpr (DUAL) acc1 = fmaf(a, Bw1[(int64_t)k * p.ldb + col], acc1);
+        if constexpr (B_KC) {
+          const float* brow = Bw + (int64_t)col * p.ldb;
+#pragma unroll 4
+          for (int k = 0; k < p.K; k += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(arow + k);
+            const float4 b4 = *reinterpret_cast<const float4*>(brow + k);
+            acc0 = fmaf(a4.x, b4.x, acc0);
+            acc0 = fmaf(a4.y, b4.y, acc0);
+            acc0 = fmaf(a4.z, b4.z, acc0);
+            acc0 = fmaf(a4.w, b4.w, acc0);
+          }
+        } else {
+#pragma unroll 4
+          for (int k = 0; k < p.K; k += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(arow + k);
+            const float* bk = Bw + (int64_t)k * p.ldb + col;
+            acc0 = fmaf(a4.x, bk[0], acc0);
+            acc0 = fmaf(a4.y, bk[p.ldb], acc0);
+            acc0 = fmaf(a4.z, bk[2 * (int64_t)p.ldb], acc0);
+            acc0 = fmaf(a4.w, bk[3 * (int64_t)p.ldb], acc0);
+            if constexpr (DUAL) {
+              const float* bk1 = Bw1 + (int64_t)k * p.ldb + col;
+              acc1 = fmaf(a4.x, bk1[0], acc1);
+              acc1 = fmaf(a4.y, bk1[p.ldb], acc1);
+              acc1 = fmaf(a4.z, bk1[2 * (int64_t)p.ldb], acc1);
+              acc1 = fmaf(a4.w, bk1[3 * (int64_t)p.ldb], acc1);
+            }
+          }
         }
       }
       epilogue<EPI, false, DUAL>(p, e, gr, col, acc0, acc1);
@@ -1339,7 +1389,7 @@ template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGR
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
   static_assert(KGROUP || BM == kGemmBM || (BM == kGemmBMFew && !W4),
                 "M-grouped tiles follow the tile table");
-  const int bm = bf16 ? BM : kBMf, bn = bf16 ? BN : kBNf;
+  const int bm = bf16 ? BM : (KGROUP ? kBMfK : kBMf), bn = bf16 ? BN : kBNf;
   p.ntn = (p.N + bn - 1) / bn;
   int blocks;
   if (KGROUP) {
