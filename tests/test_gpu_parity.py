@@ -276,7 +276,10 @@ def test_zero_tokens():
     ("c3_zipf_small_accum", "c3", dict(S=257, H=256, Hf=256), L.MOE_F_RENORM),
     ("c2_multi_tile_accum", "c2", dict(S=2100, H=256, Hf=384, E=12), L.MOE_F_RENORM),
     ("c2_raw_gates_recompute_accum", "c2", dict(S=300, H=256, Hf=384), L.MOE_F_RECOMPUTE),
-], ids=["c3_zipf_small_accum", "c2_multi_tile_accum", "c2_raw_gates_recompute_accum"])
+    # the fp32 kernel's accumulating epilogue (64-row weight-gradient tiles)
+    ("c1_tiny_fp32_accum", "c1", {}, L.MOE_F_RENORM),
+], ids=["c3_zipf_small_accum", "c2_multi_tile_accum", "c2_raw_gates_recompute_accum",
+        "c1_tiny_fp32_accum"])
 def test_accumulated_weight_gradients(cid, cfg, ov, flags):
     """MOE_F_ACCUM_GRAD adds the step's weight gradients to what the buffers hold.
 
