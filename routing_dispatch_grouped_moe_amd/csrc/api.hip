@@ -103,14 +103,10 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t f
   return L;
 }
 
-}  // namespace moe
-
-using namespace moe;
-
 // -------------------------------------------------------------- validation --
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static moe_status_t check_dims(const moe_dims_t* d) {
+moe_status_t check_dims(const moe_dims_t* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (d->S < 0 || d->H <= 0 || d->Hf <= 0 || d->E <= 0 || d->K <= 0) return MOE_ERR_SHAPE;
@@ -122,13 +118,17 @@ static moe_status_t check_dims(const moe_dims_t* d) {
   return MOE_OK;
 }
 
-static moe_status_t check_ptrs(std::initializer_list<const void*> ps) {
+moe_status_t check_ptrs(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (!p) return MOE_ERR_NULL;
   for (const void* p : ps)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
+
+}  // namespace moe
+
+using namespace moe;
 
 static moe_status_t check_ws(const moe_dims_t* d, const void* ws, size_t ws_bytes) {
   if (!ws) return MOE_ERR_NULL;
@@ -227,9 +227,10 @@ moe_status_t moe_dispatch(const moe_dims_t* d, const void* x, const int32_t* top
   else MOE_TRY(check_ptrs({x, topk_idx, cu_seqlens, row_of, tok_of, xd}));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   const WsLayout L = ws_layout(d->S, d->H, d->Hf, d->E, d->K, d->dtype, d->flags);
-  launch_dispatch(x, topk_idx, cu_seqlens, row_of, tok_of, xd, L, reinterpret_cast<char*>(ws),
-                  d->S, d->H, d->E, d->K, d->dtype == MOE_BF16,
-                  reinterpret_cast<hipStream_t>(stream));
+  char* w = reinterpret_cast<char*>(ws);
+  launch_dispatch(x, topk_idx, cu_seqlens, row_of, tok_of, xd, L, w,
+                  reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, d->K,
+                  d->dtype == MOE_BF16, reinterpret_cast<hipStream_t>(stream));
   return launched();
 }
 

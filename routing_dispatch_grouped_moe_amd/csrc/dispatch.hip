@@ -9,7 +9,8 @@
 //               in an LDS bitmap for every pair (order-free ds_or), then
 //               stores the bitmap and the per-expert popcounts.
 //   2. scan:    one block turns the [block, expert] counts into cu_seqlens
-//               and the first row of every (block, expert) run.
+//               and the first row of every (block, expert) run (the count
+//               table staged in LDS by one round of coalesced loads).
 //   3. scatter: one wavefront per token.  The rank of token s inside its
 //               expert's run is the popcount of the bitmap bits below s, so
 //               rows come out in ascending token order (bit-exact, unique).
@@ -21,7 +22,7 @@
 
 namespace moe {
 
-constexpr int kDispTok = 256;  // tokens per bitmap block (8 words of 32 bits)
+constexpr int kDispTok = kDispatchTokens;  // tokens per bitmap block (8 words of 32 bits)
 
 __global__ __launch_bounds__(256) void dispatch_bits_kernel(const int32_t* __restrict__ idx,
                                                             uint32_t* __restrict__ bits_g,
@@ -72,14 +73,49 @@ __device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
   return incl - v;
 }
 
+// Counts of every (block, expert) -> cu_seqlens and the first row of every
+// (block, expert) run.  With the whole [nb][E] count table in LDS (it is
+// loaded in one round of independent coalesced loads, eight per thread in
+// flight), thread e scans its expert's column there, a block scan over the
+// experts gives cu, and the bases leave as coalesced rows.  Tables larger
+// than the LDS budget take the per-thread column walk through global memory.
+constexpr int kScanLdsInts = 32768;  // 128 KB of dynamic LDS
+
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
                                                              int32_t* __restrict__ base,
                                                              int32_t* __restrict__ cu, int nb,
                                                              int E) {
+  extern __shared__ int tab[];  // [nb][E] when it fits
   __shared__ int sh[1024];
+  __shared__ int start_e[1024];
   const int e = threadIdx.x;
+  const bool in_lds = (int64_t)nb * E <= kScanLdsInts;
+  const int n = in_lds ? nb * E : 0;
   int tot = 0;
-  if (e < E) {
+  if (in_lds) {
+    for (int i0 = 0; i0 < n; i0 += 8 * 1024) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024 + e;
+        v[u] = i < n ? hist[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024 + e;
+        if (i < n) tab[i] = v[u];
+      }
+    }
+    __syncthreads();
+    if (e < E) {
+      // exclusive prefix of the column, in place
+      for (int b = 0; b < nb; ++b) {
+        const int c = tab[b * E + e];
+        tab[b * E + e] = tot;
+        tot += c;
+      }
+    }
+  } else if (e < E) {
     for (int b = 0; b < nb; ++b) {
       const int c = hist[(size_t)b * E + e];
       base[(size_t)b * E + e] = tot;
@@ -87,12 +123,18 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     }
   }
   int all;
-  const int start = block_exclusive_scan_1024(e < E ? tot : 0, sh, &all);
+  const int start = block_exclusive_scan_1024(e < E ? tot : 0, sh, &all);  // its barriers publish tab
   if (e < E) {
     cu[e] = start;
-    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += start;
+    start_e[e] = start;
   }
   if (e == 0) cu[E] = all;
+  __syncthreads();
+  if (in_lds) {
+    for (int i = e; i < n; i += 1024) base[i] = tab[i] + start_e[i % E];
+  } else if (e < E) {
+    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += start;
+  }
 }
 
 template <bool BF16>
@@ -147,9 +189,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 }
 
 void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
-                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
-                     int E, int K, bool bf16, hipStream_t s) {
-  uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
+                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, uint32_t* status,
+                     int64_t S, int H, int E, int K, bool bf16, hipStream_t s) {
   uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
   int32_t* base = reinterpret_cast<int32_t*>(ws + L.base);
@@ -160,8 +201,15 @@ void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* ro
                        hist, status, (int)S, E, K);
   }
   {
+    const size_t lds = (size_t)nb * E <= (size_t)kScanLdsInts ? (size_t)nb * E * 4 : 0;
+    // a failure stays the thread's last HIP error (the entry point reports it)
+    static bool attr = false;
+    if (!attr)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(dispatch_scan_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kScanLdsInts * 4) == hipSuccess;
     TimedLaunch tl("dispatch_scan", s);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, hist, base, cu, nb, E);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), lds, s, hist, base, cu, nb, E);
   }
   if (S > 0) {
     TimedLaunch tl("dispatch_scatter", s);

@@ -6,7 +6,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
+#include "moe.h"
+
 namespace moe {
+
+// Host-side argument checks shared by the entry points (api.hip): the size
+// contract of include/moe.h, and non-null 16-byte-aligned pointers.
+moe_status_t check_dims(const moe_dims_t* d);
+moe_status_t check_ptrs(std::initializer_list<const void*> ps);
 
 // Kernel timer hook: when the library timer is on, launches are bracketed by
 // events recorded on the launch stream.
@@ -68,9 +77,12 @@ void launch_route(const void* x, const void* wgT, const float* bias, float* logi
 
 void launch_load_stats(const int32_t* counts, int E, float* stats, hipStream_t s);
 
+// status: where the kernels OR their anomaly bits (the workspace's status word,
+// or the caller's word for the allocation-free entry point)
 void launch_dispatch(const void* x, const int32_t* idx, int32_t* cu, int32_t* row_of,
-                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, int64_t S, int H,
-                     int E, int K, bool bf16, hipStream_t s);
+                     int32_t* tok_of, void* xd, const WsLayout& L, char* ws, uint32_t* status,
+                     int64_t S, int H, int E, int K, bool bf16, hipStream_t s);
+constexpr int kDispatchTokens = 256;  // tokens per dispatch bitmap block
 
 // M tiles of every expert; with expert_order also the experts by descending
 // row count into the eorder region (used by the weight-gradient products)

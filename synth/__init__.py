@@ -14,5 +14,6 @@ from .inputs import (  # noqa: F401
     make_workload,
     device_expert_weights,
     host_expert_weights,
+    router_bias,
     zipf_bias,
 )

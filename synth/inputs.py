@@ -180,6 +180,30 @@ def maxvio_bias(target: float) -> Optional[np.ndarray]:
     return None if vec is None else np.asarray(vec, dtype=np.float32)
 
 
+def router_bias(cfg: dict, *, maxvio: Optional[float] = None, beta: Optional[float] = None):
+    """(bias [E] float32 or None, beta) of a workload's router at a load-skew level.
+
+    "zipf": the fixed Zipf(s) skew; "maxvio": the stored balancing bias for a
+    level below the unbiased router's own skew, else -beta*ln(1+pi(e)) with
+    beta from the stored table (beta = 0, the balanced case, when no level is
+    asked for); "none": no bias.
+    """
+    E, seed = cfg["E"], cfg["seed"]
+    if cfg["bias"] == "zipf":
+        return zipf_bias(E, cfg["zipf_s"], seed), 0.0
+    if cfg["bias"] != "maxvio":
+        return None, 0.0
+    if beta is None and maxvio is not None and maxvio_bias(maxvio) is not None:
+        bias = maxvio_bias(maxvio)
+        if bias.shape[0] != E:
+            raise ValueError("stored balancing bias does not match E")
+        return bias, 0.0
+    if beta is None:
+        beta = maxvio_beta(maxvio) if maxvio is not None else 0.0
+    b = float(beta)
+    return (zipf_bias(E, b, seed) if b != 0.0 else np.zeros(E, np.float32)), b
+
+
 def make_workload(name: str, *, S: Optional[int] = None, beta: Optional[float] = None,
                   maxvio: Optional[float] = None, host_weights: Optional[bool] = None,
                   H: Optional[int] = None, Hf: Optional[int] = None,
@@ -211,20 +235,7 @@ def make_workload(name: str, *, S: Optional[int] = None, beta: Optional[float] =
     Wg = _normal(seed, T_WG, 0, (Hd, Ed), cfg["w_std"], dt)
     dout = _normal(seed, T_DOUT, 0, (S_in, Hd), 1.0, dt)
 
-    bias = None
-    b = 0.0
-    if cfg["bias"] == "zipf":
-        bias = zipf_bias(Ed, cfg["zipf_s"], seed)
-    elif cfg["bias"] == "maxvio" and beta is None and maxvio is not None \
-            and maxvio_bias(maxvio) is not None:
-        bias = maxvio_bias(maxvio)
-        if bias.shape[0] != Ed:
-            raise ValueError("stored balancing bias does not match E")
-    elif cfg["bias"] == "maxvio":
-        if beta is None:
-            beta = maxvio_beta(maxvio) if maxvio is not None else 0.0
-        b = float(beta)
-        bias = zipf_bias(Ed, b, seed) if b != 0.0 else np.zeros(Ed, np.float32)
+    bias, b = router_bias(cfg, maxvio=maxvio, beta=beta)
     w_r = _normal(seed, T_WR, 0, (Hd,), cfg["w_std"], dt) if mod else None
 
     wl = Workload(cfg=cfg, S=cfg["S"], H=Hd, Hf=Hfd, E=Ed, K=Kd, dtype=dt, x=x, Wg=Wg,
