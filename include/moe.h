@@ -156,6 +156,28 @@ moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const int32_t* 
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_dispatch_noalloc - moe_dispatch without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same inputs, outputs and results
+ * (bit for bit) as moe_dispatch; the dispatch kernels' per-block bitmaps,
+ * counts and bases live in a scratch array the library holds on each GPU it
+ * runs on (MOE_DISPATCH_NOALLOC_SCRATCH_BYTES, kept until the process ends).
+ * The call allocates nothing.
+ *   status  optional device uint32: the MOE_DEV_* anomaly bits are OR-ed into
+ *           it (it accumulates until the caller clears it); NULL: not reported
+ * Limit: 256 + 40 * ceil(S / 256) * E bytes (each region rounded up to 256)
+ * must fit the scratch, i.e. about ceil(S / 256) * E <= 104 800 (S up to
+ * 26 112 at E = 1024, 69 888 at E = 384); larger sizes return
+ * MOE_ERR_WORKSPACE before anything is launched.  Every call on one GPU reuses that GPU's
+ * scratch: calls that overlap on one GPU (different streams or threads) race
+ * and must be serialised by the caller.
+ */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status_t moe_dispatch_noalloc(const moe_dims_t* dims, const void* x, const int32_t* topk_idx,
+                                  int32_t* cu_seqlens, int32_t* row_of, int32_t* tok_of, void* xd,
+                                  uint32_t* status, void* stream);
+
+/*
  * moe_grouped_ffn - the grouped SwiGLU expert FFN over all experts' rows.
  * [T4] "RMSNorm, RoPE, SwiGLU" table, SwiGLU row (three matrix products);
  * [MEP] guide, weights step (one contiguous [E, H, H'] tensor per projection;

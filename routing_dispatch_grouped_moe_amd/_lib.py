@@ -26,8 +26,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 # Every entry point include/moe.h declares (checked by the CPU test suite).
 EXPORTS = (
     "moe_workspace_bytes", "moe_clear_status", "moe_status_string", "moe_read_status",
-    "moe_route", "moe_load_stats", "moe_dispatch", "moe_grouped_ffn", "moe_ffn_up", "moe_ffn_down",
-    "moe_combine", "moe_backward", "moe_mod_workspace_bytes", "moe_mod_select",
+    "moe_route", "moe_load_stats", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn",
+    "moe_ffn_up", "moe_ffn_down", "moe_combine", "moe_backward", "moe_mod_workspace_bytes", "moe_mod_select",
     "moe_mod_merge", "moe_mod_backward", "moe_timer_enable", "moe_timer_reset",
     "moe_timer_read",
 )
@@ -75,6 +75,7 @@ def load():
         "moe_read_status": (I32, [P, C.POINTER(U32), P]),
         "moe_route": (I32, [D, P, P, P, P, P, P, P, P, S, P]),
         "moe_dispatch": (I32, [D, P, P, P, P, P, P, P, S, P]),
+        "moe_dispatch_noalloc": (I32, [D, P, P, P, P, P, P, P, P]),
         "moe_load_stats": (I32, [I32, P, P, P]),
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_ffn_up": (I32, [D, P, P, P, P, P, P, P, P, S, P]),
@@ -147,6 +148,13 @@ def moe_dispatch(d, x, topk_idx, cu_seqlens, row_of, tok_of, xd, ws):
     _check("moe_dispatch", load().moe_dispatch(C.byref(d), _p(x), _p(topk_idx), _p(cu_seqlens),
                                                _p(row_of), _p(tok_of), _p(xd), _p(ws),
                                                ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_dispatch_noalloc(d, x, topk_idx, cu_seqlens, row_of, tok_of, xd, status=None):
+    """moe_dispatch on the library's own scratch (no workspace); status: optional device uint32."""
+    _check("moe_dispatch_noalloc", load().moe_dispatch_noalloc(
+        C.byref(d), _p(x), _p(topk_idx), _p(cu_seqlens), _p(row_of), _p(tok_of), _p(xd),
+        _p(status), _stream()))
 
 
 def moe_grouped_ffn(d, xd, cu_seqlens, W1, W3, W2, h1, h3, a, y, ws):

@@ -126,6 +126,25 @@ def test_other_entry_points_reject_before_launch(L):
     assert L.moe_mod_workspace_bytes(4096) > 0
 
 
+def test_dispatch_noalloc_rejects_before_launch(L):
+    """The allocation-free dispatch validates like moe_dispatch and refuses sizes past its scratch."""
+    lib = _raw(L)
+    f = lib.moe_dispatch_noalloc
+    d = L.dims(8192, 7168, 2048, 384, 8, "bf16")
+    assert f(C.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(C.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, None, None) == 4
+    assert f(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.c_void_p((1 << 20) + 2), None) == 4
+    assert f(C.byref(L.dims(64, 100, 128, 8, 2, "bf16")), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None, None) == 6
+    # scratch limit: 256 + 40 * ceil(S / 256) * E bytes (regions rounded to 256) <= 4 MiB;
+    # only sizes past it are passed here (a size that fits would go on to launch, which
+    # the GPU test covers at the boundary itself)
+    for S, E in ((26113, 1024), (69889, 384), (2 ** 22, 64), (2 ** 22, 8)):
+        st = f(C.byref(L.dims(S, 128, 128, E, 2, "bf16")), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+               None, None)
+        assert st == 5, (S, E, st)
+
+
 def test_status_strings(L):
     lib = _raw(L)
     for code, name in [(0, b"ok"), (5, b"workspace too small"), (7, b"HIP launch error")]:
