@@ -44,3 +44,26 @@ def test_roofline_entry_picks_the_binding_peak():
     assert up["bound"] == "mfma" and up["unit"] == "TFLOP/s" and 0 < up["frac"] < 1
     comb = bench.roofline_entry("combine", cfg, counts, 40e-6, True)
     assert comb["bound"] == "hbm" and comb["unit"] == "GB/s" and 0 < comb["frac"] < 1
+
+
+def test_whole_call_models_at_the_384_expert_shape():
+    # what each C-ABI call as a whole must move (its set-up kernels add no
+    # algorithmic bytes)
+    cfg = dict(S=8192, H=7168, Hf=2048, E=384, K=8, dtype="bf16")
+    counts = [8192 * 8 // 384] * 384
+    S, H, E, K, R = 8192, 7168, 384, 8, 8192 * 8
+    _, disp = bench.kernel_model("call:moe_dispatch", cfg, counts)
+    assert disp == 4 * S * K + S * H * 2 + R * H * 2 + 8 * R + 4 * (E + 1)
+    assert abs(disp / 8e12 * 1e6 - 132.2) < 0.5          # about 132 us at 8 TB/s
+    _, comb = bench.kernel_model("call:moe_combine", cfg, counts)
+    assert comb == R * H * 2 + S * H * 2 + 8 * S * K
+    f, rb = bench.kernel_model("call:moe_route", cfg, counts)
+    assert f == 2 * S * H * E and rb == S * H * 2 + H * E * 2 + 4 * S * E + 8 * S * K + 4 * E
+    # route at this shape is MFMA-bound by its algorithmic figures (on the ridge)
+    assert bench.roofline_entry("call:moe_route", cfg, counts, 100e-6, True)["bound"] == "mfma"
+
+
+def test_median():
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 3.0, 2.0]) == 2.5
+    assert bench.median([]) is None
