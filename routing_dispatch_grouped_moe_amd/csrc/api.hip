@@ -3,6 +3,8 @@
 // contract of every entry point are in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <string.h>
+
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -155,7 +157,11 @@ size_t moe_workspace_bytes(const moe_dims_t* d) {
 }
 
 const char* moe_status_string(moe_status_t st) {
-  switch (st) {
+  // a C caller may pass any int: read the bits, not an enum value outside the
+  // enumerators' range (undefined in C++)
+  int32_t code;
+  memcpy(&code, &st, sizeof code);
+  switch (code) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "null pointer";
     case MOE_ERR_SHAPE: return "invalid shape";

@@ -7,11 +7,11 @@
 //
 // gfx950 design: scores and every row copy run one wavefront per token with
 // 16-byte pieces; the per-sequence selection runs in one 1024-thread block
-// per sequence: 64-bit order keys (score bits : ~position) in LDS, each
-// token's rank counted against all keys of its sequence, then an LDS scan
-// of the keep flags gives the ascending kept order.  The merge and the
-// backward find a token's kept slot by binary search in its sequence's
-// ascending keep list.
+// per sequence: 64-bit order keys (score bits : ~position) in LDS, a
+// bitonic sort of them (descending), the first C positions marked in an LDS
+// bitmap, then a block scan of per-thread counts writes them out in
+// ascending position order.  The merge and the backward find a token's kept
+// slot by binary search in its sequence's ascending keep list.
 #include "dev_common.h"
 #include "launch.h"
 #include "moe.h"
