@@ -80,6 +80,11 @@ def check_against_oracle(wl, got, tol, backward=True, renorm=True):
                        ("dh3", "dh3"), ("dxd", "dxd"), ("dx", "dx"), ("dWg", "dWg"),
                        ("dW1", "dW1"), ("dW3", "dW3"), ("dW2", "dW2")):
             errs[n] = assert_close(n, got[n], bw[key], tol)
+        # each expert's weight gradient against its own scale (a cold
+        # expert's error must not hide under a hot expert's maximum)
+        for n in ("dW1", "dW3", "dW2"):
+            for e in np.nonzero(fw["counts"] > 0)[0]:
+                errs[f"{n}[{e}]"] = assert_close(f"{n}[{e}]", got[n][e], bw[n][e], tol)
     # end-to-end routing: the oracle's own logits vs the GPU's choice
     own = oracle.topk_experts(want_logits, K)
     flips = int(np.sum(np.any(own != got["topk_idx"], axis=1)))
@@ -316,6 +321,22 @@ def test_accumulated_weight_gradients(cid, cfg, ov, flags):
     for n in ("dW1", "dW3", "dW2", "dWg"):
         got = to_host(getattr(layer, n)).astype(np.float64) - pats[n]
         assert_close(f"{n} increment", got, bw[n], BF16_TOL)
+    if dt == "f32":
+        # The fp32 kernels accumulate each output in one fmaf chain and the
+        # accumulating epilogue adds that chain's result to the old value
+        # once, so dW must be float32(P + G) bit for bit, with G the
+        # overwriting run's gradient (the same chain): the fp32 bar without
+        # the cancellation of subtracting P.
+        over = MoELayer(wl.S, wl.H, wl.Hf, wl.E, wl.K, dt, flags=flags)
+        over.forward(x, Wg, b, W1, W3, W2)
+        over.backward(dout, x, Wg, W1, W3, W2)
+        torch.cuda.synchronize()
+        for n in ("dW1", "dW3", "dW2", "dWg"):
+            G = to_host(getattr(over, n)).astype(np.float32)
+            want = pats[n].astype(np.float32) + G
+            np.testing.assert_array_equal(to_host(getattr(layer, n)), want,
+                                          err_msg=f"{n}: P + G in fp32, bit for bit")
+            assert_close(f"{n} (overwrite)", G, bw[n], F32_TOL)
     for n in ("dW1", "dW3", "dW2"):
         np.testing.assert_array_equal(to_host(getattr(layer, n))[wl.E - 1], pats[n][wl.E - 1],
                                       err_msg=f"{n}: an expert without rows must keep its values")
