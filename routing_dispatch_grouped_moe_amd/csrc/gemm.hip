@@ -708,6 +708,10 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // those reads wait for the loads
   __shared__ __attribute__((aligned(1024))) char stage0[kStage];
   __shared__ __attribute__((aligned(1024))) char stage1[kStage];
+  // the third buffer of the B operand (the first two follow the A tiles in
+  // stage0 and stage1): 160 KB in all, the whole LDS of a compute unit
+  __shared__ __attribute__((aligned(1024))) char stage2[NB * kTileB];
+  static_assert(2 * kStage + NB * kTileB <= 160 * 1024, "LDS of one compute unit");
 
   // products with a plain store epilogue split the tiles of a partial last
   // wave along K (fp32 partial tiles, summed by tail_reduce_kernel)
@@ -725,6 +729,16 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
+  // 32-row block of the tile that the wavefront's row block i is.  M-grouped
+  // tiles interleave the two wavefront rows (blocks wm, wm + 2, ...), and an
+  // expert's last, partial tile runs MFMAs only over the blocks that hold
+  // valid rows (mi_act per wavefront): with 171 rows both wavefront rows
+  // take 3 blocks where contiguous halves would give one of them 4.  The
+  // K-grouped tiles (M is not rows there) keep contiguous halves, all active.
+  auto blk = [&](int i) { return KGROUP ? wm * MI + i : 2 * i + wm; };
+  int mi_act = MI;
+  if constexpr (!KGROUP)
+    mi_act = __builtin_amdgcn_readfirstlane(min(MI, max(0, ((valid + 31) / 32 - wm + 1) / 2)));
 
   // operand bases (A segments, B operands) and their byte ranges
   const uint16_t* a_ptr[TWOSEG ? 2 : 1];
@@ -783,10 +797,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     }
   };
   constexpr int kDmaA = DmaOperand<A_KC, BM, 1, 4>::kPer;
-  auto issue_one = [&](int t, const u32x4 (&ra)[1], const u32x4 (&rb)[NB], char* st) {
-    if (t < kDmaA) da.issue_one(t, ra, st, w);
-    else db.issue_one(t - kDmaA, rb, st + kTileA, w);
-  };
+  constexpr int kDmaB = DmaOperand<B_KC, BN, NB, 4>::kPer;
   f32x16 acc[NB][MI][NJ];
 #pragma unroll
   for (int q = 0; q < NB; ++q)
@@ -802,80 +813,112 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // per-lane LDS bases of the transposed fragments (loop invariant)
   uint32_t abase[MI], bbase[NJ];
 #pragma unroll
-  for (int f = 0; f < MI; ++f) abase[f] = frag_km_base<BM>(wm * WM + f * 32, lane);
+  for (int f = 0; f < MI; ++f) abase[f] = frag_km_base<BM>(blk(f) * 32, lane);
 #pragma unroll
   for (int f = 0; f < NJ; ++f) bbase[f] = frag_km_base<BN>(wn * WN + f * 32, lane);
-  auto read_frag = [&](const char* st, int kk, int f, u32x4 (&af)[MI], u32x4 (&bfr)[NB][NJ]) {
+  // sa: the A tile of the step, sb: its B buffer; act: the row blocks with
+  // MFMA work (fragments of the others are not read)
+  auto read_frag = [&](const char* sa, const char* sb, int kk, int f, u32x4 (&af)[MI],
+                       u32x4 (&bfr)[NB][NJ], int act) {
     if (f < MI) {
-      if constexpr (A_KC) af[f] = frag_kc(st, wm * WM + f * 32, kk, lane);
-      else af[f] = frag_km_at<BM>(st, abase[f], kk);
+      if (KGROUP || f < act) {
+        if constexpr (A_KC) af[f] = frag_kc(sa, blk(f) * 32, kk, lane);
+        else af[f] = frag_km_at<BM>(sa, abase[f], kk);
+      }
     } else {
       const int q = (f - MI) / NJ, j = (f - MI) % NJ;
-      const char* t = st + kTileA + q * kTileB;
+      const char* t = sb + q * kTileB;
       if constexpr (B_KC) bfr[q][j] = frag_kc(t, wn * WN + j * 32, kk, lane);
       else bfr[q][j] = frag_km_at<BN>(t, bbase[j], kk);
     }
   };
   constexpr int kMfma = MI * NB * NJ;
   constexpr int kFrag = MI + NB * NJ;
-  constexpr int kDma = kDmaA + DmaOperand<B_KC, BN, NB, 4>::kPer;
-  constexpr int kHalf = kDma / 2;
-  static_assert(kFrag <= kMfma && kHalf <= kMfma && kMfma % kHalf == 0, "slice interleave");
+  // B loads of a step spread over slices 0-2 (kB0, kB1, the rest), A loads
+  // over slice 3
+  constexpr int kB0 = (kDmaB + 2) / 3, kB1 = (kDmaB + 1) / 3, kB2 = kDmaB - kB0 - kB1;
+  static_assert(kFrag <= kMfma && kDmaA <= kMfma && kB0 <= kMfma, "slice interleave");
 
   // One K16 slice in a pinned issue order: MFMA t on the current fragments,
-  // then fragment t of the next slice (from stage rd), then every
-  // (kMfma / kHalf)-th MFMA one direct load (instruction d0 + n of the step
-  // whose descriptors are ra/rb, into stage ds).  The address unit accepts
-  // one such 1-KB load about every 16 cycles, so a step's loads are spread
-  // over two slices rather than bunched.
-  auto slice = [&](const u32x4 (&afc)[MI], const u32x4 (&bfc)[NB][NJ], const char* rd, int rd_kk,
-                   u32x4 (&afn)[MI], u32x4 (&bfn)[NB][NJ], const u32x4 (&ra)[1],
-                   const u32x4 (&rb)[NB], char* ds, int d0, auto dma_tag) {
-    constexpr bool DMA = decltype(dma_tag)::value;
+  // then fragment t of the next slice (from A tile ra_t and B buffer rb_t),
+  // then, spread evenly over the slice's MFMAs, its n direct loads:
+  // instructions d0 .. d0+n-1 of operand OP (0: A, 1: B) of the step whose
+  // descriptors are rs, into LDS at ds.  The address unit accepts one such
+  // 1-KB load about every 16 cycles, so a step's loads are not bunched.
+  auto slice = [&](const u32x4 (&afc)[MI], const u32x4 (&bfc)[NB][NJ], const char* ra_t,
+                   const char* rb_t, int rd_kk, u32x4 (&afn)[MI], u32x4 (&bfn)[NB][NJ],
+                   const u32x4* rs, char* ds, int d0, auto act_tag, auto op_tag, auto n_tag) {
+    constexpr int OP = decltype(op_tag)::value, N = decltype(n_tag)::value;
+    constexpr int act = decltype(act_tag)::value;
 #pragma unroll
     for (int t = 0; t < kMfma; ++t) {
       const int i = t / (NB * NJ), q = (t / NJ) % NB, j = t % NJ;
-      acc[q][i][j] = kSwapAB
-          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfc[q][j]),
-                                                    __builtin_bit_cast(bf16x8, afc[i]), acc[q][i][j],
-                                                    0, 0, 0)
-          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, afc[i]),
-                                                    __builtin_bit_cast(bf16x8, bfc[q][j]),
-                                                    acc[q][i][j], 0, 0, 0);
-      if (rd != nullptr && t < kFrag) read_frag(rd, rd_kk, t, afn, bfn);
-      if constexpr (DMA)
-        if (t % (kMfma / kHalf) == 0) issue_one(d0 + t / (kMfma / kHalf), ra, rb, ds);
+      if (i < act)
+        acc[q][i][j] = kSwapAB
+            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfc[q][j]),
+                                                      __builtin_bit_cast(bf16x8, afc[i]),
+                                                      acc[q][i][j], 0, 0, 0)
+            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, afc[i]),
+                                                      __builtin_bit_cast(bf16x8, bfc[q][j]),
+                                                      acc[q][i][j], 0, 0, 0);
+      // (no null test on the tile pointers: LDS address 0 is a valid
+      // address, so the compiler would keep it as a branch between MFMAs)
+      if (t < kFrag) read_frag(ra_t, rb_t, rd_kk, t, afn, bfn, act);
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        if (t == n * kMfma / N) {
+          if constexpr (OP == 0) {
+            const u32x4 r1[1] = {rs[0]};
+            da.issue_one(d0 + n, r1, ds, w);
+          } else {
+            u32x4 rn[NB];
+#pragma unroll
+            for (int o = 0; o < NB; ++o) rn[o] = rs[o];
+            db.issue_one(d0 + n, rn, ds, w);
+          }
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using T = std::true_type;
-  using F = std::false_type;
+  using IA = std::integral_constant<int, 0>;
+  using IB = std::integral_constant<int, 1>;
+  using NA = std::integral_constant<int, kDmaA>;
+  using N0 = std::integral_constant<int, kB0>;
+  using N1 = std::integral_constant<int, kB1>;
+  using N2 = std::integral_constant<int, kB2>;
 
-  // Step kt (stage CUR holds its data; the first half of step kt+1's loads
-  // are in flight):
-  //   slice 0   second half of step kt+1's loads into the other stage
-  //   slices 1-2
-  //   barrier   after this wavefront's loads of step kt+1 landed (vmcnt)
-  //   slice 3   first half of step kt+2's loads into stage CUR, which every
-  //             wavefront finished reading before the barrier
+  // The A tiles (activation rows, mostly L2 hits) take two stages, the B
+  // tiles (the expert weights, streamed from HBM when an expert has few rows)
+  // three buffers, so B is fetched two steps ahead.  Step kt (local index i,
+  // A tile in stage CUR, B in buffer i % 3; A(kt+1) and B(kt+1) in flight):
+  //   slices 0-2  B(kt+2) into buffer (i+2) % 3, last read in step kt-1
+  //   barrier     after everything but those loads landed (vmcnt(kDmaB):
+  //               loads complete in issue order), i.e. A(kt+1), B(kt+1)
+  //   slice 3     A(kt+2) into stage CUR, which every wavefront finished
+  //               reading before the barrier
   // Loads past the last step stay inside the descriptors' ranges and go to
-  // a stage that is not read again, so the loop has no tail copy; the step
+  // tiles that are not read again, so the loop has no tail copy; the step
   // count is rounded up to even for the two-stage unroll (K-grouped products
   // then run one step of zero rows when their row count needs an odd number).
-  auto step = [&](int kt, auto cur_tag) {
+  char* const bbuf0 = stage0 + kTileA;
+  char* const bbuf1 = stage1 + kTileA;
+  auto bsel = [&](int i) -> char* { return i == 0 ? bbuf0 : (i == 1 ? bbuf1 : stage2); };
+  auto step = [&](int kt, int i3, auto cur_tag, auto act) {
     constexpr int CUR = decltype(cur_tag)::value;
     char* cur = CUR ? stage1 : stage0;
     char* nxt = CUR ? stage0 : stage1;
-    u32x4 ra1[1], rb1[NB], ra2[1], rb2[NB];
-    step_rsrc(kt + 1, ra1, rb1);
+    char* bc = bsel(i3);
+    char* bn = bsel(i3 == 2 ? 0 : i3 + 1);
+    char* bnn = bsel(i3 == 0 ? 2 : i3 - 1);
+    u32x4 ra2[1], rb2[NB];
     step_rsrc(kt + 2, ra2, rb2);
-    slice(af0, bf0, cur, 1, af1, bf1, ra1, rb1, nxt, kHalf, T{});
-    slice(af1, bf1, cur, 2, af0, bf0, ra1, rb1, nxt, 0, F{});
-    slice(af0, bf0, cur, 3, af1, bf1, ra1, rb1, nxt, 0, F{});
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    slice(af1, bf1, nxt, 0, af0, bf0, ra2, rb2, cur, 0, T{});
+    slice(af0, bf0, cur, bc, 1, af1, bf1, rb2, bnn, 0, act, IB{}, N0{});
+    slice(af1, bf1, cur, bc, 2, af0, bf0, rb2, bnn, kB0, act, IB{}, N1{});
+    slice(af0, bf0, cur, bc, 3, af1, bf1, rb2, bnn, kB0 + kB1, act, IB{}, N2{});
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaB) : "memory");
+    slice(af1, bf1, nxt, bn, 0, af0, bf0, ra2, cur, 0, act, IA{}, NA{});
   };
 
   // K steps [k_lo, k_end) of this block: all of them, or one part of a split
@@ -890,20 +933,41 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     }
   }
   {
+    // A(k_lo), B(k_lo), then B(k_lo+1), A(k_lo+1) (left in flight)
     u32x4 ra[1], rb[NB];
     step_rsrc(k_lo, ra, rb);
 #pragma unroll
-    for (int t = 0; t < kDma; ++t) issue_one(t, ra, rb, stage0);
+    for (int t = 0; t < kDmaA; ++t) da.issue_one(t, ra, stage0, w);
+#pragma unroll
+    for (int t = 0; t < kDmaB; ++t) db.issue_one(t, rb, bbuf0, w);
     step_rsrc(k_lo + 1, ra, rb);
 #pragma unroll
-    for (int t = 0; t < kHalf; ++t) issue_one(t, ra, rb, stage1);
-  }
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kHalf) : "memory");
+    for (int t = 0; t < kDmaB; ++t) db.issue_one(t, rb, bbuf1, w);
 #pragma unroll
-  for (int f = 0; f < kFrag; ++f) read_frag(stage0, 0, f, af0, bf0);
-  for (int kt = k_lo; kt < k_end; kt += 2) {
-    step(kt, I0{});
-    step(kt + 1, I1{});
+    for (int t = 0; t < kDmaA; ++t) da.issue_one(t, ra, stage1, w);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kDmaA + kDmaB) : "memory");
+#pragma unroll
+  for (int f = 0; f < kFrag; ++f) read_frag(stage0, bbuf0, 0, f, af0, bf0, mi_act);
+  // one copy of the K loop per active row-block count, without branches
+  // between its MFMAs (a wavefront takes the copy of its own count; every
+  // copy runs the same loads and barriers)
+  auto kloop = [&](auto act) {
+    int i3 = 0;
+    for (int kt = k_lo; kt < k_end; kt += 2) {
+      step(kt, i3, I0{}, act);
+      i3 = i3 == 2 ? 0 : i3 + 1;
+      step(kt + 1, i3, I1{}, act);
+      i3 = i3 == 2 ? 0 : i3 + 1;
+    }
+  };
+  if (KGROUP || mi_act == MI) {
+    kloop(std::integral_constant<int, MI>{});
+  } else if constexpr (!KGROUP && MI == 4) {
+    if (mi_act == 3) kloop(std::integral_constant<int, 3>{});
+    else if (mi_act == 2) kloop(std::integral_constant<int, 2>{});
+    else if (mi_act == 1) kloop(std::integral_constant<int, 1>{});
+    else kloop(std::integral_constant<int, 0>{});
   }
   // no direct load may still be writing LDS when the block exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -972,9 +1036,6 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     };
     using R128 = std::integral_constant<int, 128>;
     using R256 = std::integral_constant<int, 256>;
-    using R64 = std::integral_constant<int, 64>;
-    using R32 = std::integral_constant<int, 32>;
-    using R96 = std::integral_constant<int, 96>;
     using R0 = std::integral_constant<int, 0>;
 
     if constexpr (EPI == EPI_F32) {
@@ -1048,14 +1109,17 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         });
       }
     } else if constexpr (EPI == EPI_STORE) {
-      // rows 0-127 in stage 0, 128-255 in stage 1 (the wavefront row wm)
-      static_assert(NB == 1 && BM == 256, "store epilogue tile");
-      char* st = wm ? stage1 : stage0;
+      // tile rows 0-127 in stage 0, 128-255 in stage 1: row block 2i + wm of
+      // the tile goes to stage i / 2
+      static_assert(NB == 1 && BM == 256 && MI == 4, "store epilogue tile");
       StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
         constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
-        const float v[4] = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
-                            acc[0][i][j][4 * g + 3]};
-        put4(st, i * 32 + (lane & 31), wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+        if (i < mi_act) {
+          const float v[4] = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
+                              acc[0][i][j][4 * g + 3]};
+          put4(i >= 2 ? stage1 : stage0, (2 * (i & 1) + wm) * 32 + (lane & 31),
+               wn * WN + j * 32 + 8 * g + 4 * (lane >> 5), v);
+        }
       });
       __syncthreads();
       store_rows(stage0, R128{}, p.C0, 0, R128{}, R0{});
@@ -1066,15 +1130,17 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
       static_assert(NB == 2 && BM == 256 && BN == 128, "SwiGLU epilogue tile");
       StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
         constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
-        const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        float v0[4], a[4];
+        if (i < mi_act) {
+          const int r = blk(i) * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          float v0[4], a[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v0[t] = acc[0][i][j][4 * g + t];
-          a[t] = silu_f(v0[t]) * acc[1][i][j][4 * g + t];
+          for (int t = 0; t < 4; ++t) {
+            v0[t] = acc[0][i][j][4 * g + t];
+            a[t] = silu_f(v0[t]) * acc[1][i][j][4 * g + t];
+          }
+          put4(stage0, r, c, v0);
+          put4(stage1, r, c, a);
         }
-        put4(stage0, r, c, v0);
-        put4(stage1, r, c, a);
       });
       __syncthreads();
       // a null output (h1, h3 under recompute, or a when recomputing) is skipped
@@ -1084,73 +1150,82 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
         __syncthreads();
         StaticFor<0, MI * NJ * 4>::run([&](auto tag) {
           constexpr int x = decltype(tag)::value, i = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
-          const int r = wm * WM + i * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          const float v1[4] = {acc[1][i][j][4 * g], acc[1][i][j][4 * g + 1], acc[1][i][j][4 * g + 2],
-                               acc[1][i][j][4 * g + 3]};
-          put4(stage0, r, c, v1);
+          if (i < mi_act) {
+            const int r = blk(i) * 32 + (lane & 31), c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+            const float v1[4] = {acc[1][i][j][4 * g], acc[1][i][j][4 * g + 1],
+                                 acc[1][i][j][4 * g + 2], acc[1][i][j][4 * g + 3]};
+            put4(stage0, r, c, v1);
+          }
         });
         __syncthreads();
         store_rows(stage0, R256{}, p.C1, 0, R256{}, R0{});
       }
     } else {
-      // SwiGLU backward: two phases of 128 tile rows (row blocks 2ph and
-      // 2ph + 1 of both wavefront rows).  A phase's h1 rows come into stage 0
+      // SwiGLU backward: two phases of 128 tile rows, phase ph the tile rows
+      // 128 ph .. 128 ph + 127 (row blocks 2 ph and 2 ph + 1 of both
+      // wavefront rows, interleaved).  A phase's h1 rows come into stage 0
       // and its h3 rows into stage 1 by direct loads (no staging registers),
-      // dh1 and dh3 overwrite them in place and leave as whole rows.
+      // dh1 and dh3 overwrite them in place and leave as whole rows.  A tile
+      // of at most 128 valid rows has no second phase.
       static_assert(EPI == EPI_SWIGLU_BWD && NB == 1 && BM == 256 && BN == 256, "dA epilogue tile");
       static_assert(MI == 4 && RS == 512, "two 128-row phases of 256 columns");
-      // staged row q of phase ph is tile row 64 ph + q (q < 64) or
-      // 128 + 64 ph + (q - 64); wavefront w loads 32 KB of one matrix:
-      // instruction u covers staged rows 2 (32 (w & 1) + u) and the next one
+      // staged row q of phase ph is tile row 128 ph + q; wavefront w loads
+      // 32 KB of one matrix: instruction u covers staged rows
+      // 2 (32 (w & 1) + u) and the next one
       const int mat = w >> 1, hl = lane >> 5, slot = lane & 31;
       const char* xbase = reinterpret_cast<const char*>(mat ? p.X1 : p.X0) +
                           ((int64_t)row0 * p.ldc + n0) * 2;
       char* dstage = mat ? stage1 : stage0;
       auto dma_phase = [&](int ph) {
         // rows past the tile's valid ones and columns past N read zeros
-        const int64_t rows_left = (int64_t)valid - 64 * ph;
+        const int64_t rows_left = (int64_t)valid - 128 * ph;
         const int64_t lim = rows_left > 0 ? ((rows_left - 1) * p.ldc + (p.N - n0)) * 2 : 0;
-        const u32x4 rs = rsrc_words(xbase + (int64_t)64 * ph * p.ldc * 2, (uint32_t)lim);
+        const u32x4 rs = rsrc_words(xbase + (int64_t)128 * ph * p.ldc * 2, (uint32_t)lim);
 #pragma unroll
         for (int u = 0; u < 32; ++u) {
-          const int j = 32 * (w & 1) + u, q = 2 * j + hl;
-          const int r = q < 64 ? q : q + 64;  // tile row minus 64 ph
-          const uint32_t voff = ((uint32_t)r * (uint32_t)p.ldc + 8u * (uint32_t)(slot ^ (q & 15))) * 2u;
+          const int j = 32 * (w & 1) + u, q = 2 * j + hl;  // q: tile row minus 128 ph
+          const uint32_t voff = ((uint32_t)q * (uint32_t)p.ldc + 8u * (uint32_t)(slot ^ (q & 15))) * 2u;
           dma16(rs, voff, dstage + j * 1024);
         }
       };
       dma_phase(0);
       StaticFor<0, 2>::run([&](auto ph_tag) {
         constexpr int ph = decltype(ph_tag)::value;
+        if (ph == 1 && valid <= 128) return;  // uniform over the block
         // this wavefront's loads (and, from the second phase on, its stores
         // of the previous one) are done; after the barrier everyone's are
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         StaticFor<0, 2 * NJ * 4>::run([&](auto x_tag) {
           constexpr int x = decltype(x_tag)::value, ib = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
           constexpr int i = 2 * ph + ib;
-          const int q = wm * 64 + ib * 32 + (lane & 31);
-          const int c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          float z[4], u[4], d1[4], d3[4];
-          get4(stage0, q, c, z);
-          get4(stage1, q, c, u);
+          if (i < mi_act) {
+            // tile row block 2 i + wm = 4 ph + 2 ib + wm
+            const int q = (2 * ib + wm) * 32 + (lane & 31);
+            const int c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+            float z[4], u[4], d1[4], d3[4];
+            get4(stage0, q, c, z);
+            get4(stage1, q, c, u);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float v = acc[0][i][j][4 * g + t];
-            const float sg = sigmoid_f(z[t]);
-            const float vs = v * sg;
-            d3[t] = vs * z[t];
-            d1[t] = vs * u[t] * (1.0f + z[t] - z[t] * sg);
+            for (int t = 0; t < 4; ++t) {
+              const float v = acc[0][i][j][4 * g + t];
+              const float sg = sigmoid_f(z[t]);
+              const float vs = v * sg;
+              d3[t] = vs * z[t];
+              d1[t] = vs * u[t] * (1.0f + z[t] - z[t] * sg);
+            }
+            put4(stage0, q, c, d1);
+            put4(stage1, q, c, d3);
           }
-          put4(stage0, q, c, d1);
-          put4(stage1, q, c, d3);
         });
         __syncthreads();
-        store_rows(stage0, R128{}, p.C0, 64 * ph, R64{}, R64{});
-        store_rows(stage1, R128{}, p.C1, 64 * ph, R64{}, R64{});
+        store_rows(stage0, R128{}, p.C0, 128 * ph, R128{}, R0{});
+        store_rows(stage1, R128{}, p.C1, 128 * ph, R128{}, R0{});
         if constexpr (ph == 0) {
-          // every wavefront has read the stages for its stores
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          dma_phase(1);
+          if (valid > 128) {
+            // every wavefront has read the stages for its stores
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            dma_phase(1);
+          }
         }
       });
     }
@@ -1162,7 +1237,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
       if (c < p.N) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int r = blk(i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const float v1 = DUAL ? acc[NB - 1][i][j][v] : 0.f;
           if constexpr (KGROUP) {
             if (m0 + r < p.M) epilogue<EPI, true, DUAL>(p, e, m0 + r, c, acc[0][i][j][v], v1);
@@ -1179,7 +1254,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
 // Sums the K parts of each split tile (in part order) and stores the bf16
 // result.  Block (tile tt, 32-row group i); thread (w, lane) takes the
 // accumulators that wavefront w, lane held in the GEMM: row
-// (w / 2) * WM + 32 i + lane % 32, columns (w % 2) * WN + 32 j + 8 g + 4 (lane / 32) + t.
+// 32 (2 i + w / 2) + lane % 32, columns (w % 2) * WN + 32 j + 8 g + 4 (lane / 32) + t.
 template <int BM, int BN, bool TWOSEG>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NJ = WN / 32;
@@ -1193,7 +1268,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
   const int64_t row0 = (int64_t)p.cu[tl.x] + tl.y;
   const int valid = min(BM, p.cu[tl.x + 1] - (int)row0);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int r = (w >> 1) * WM + i * 32 + (lane & 31);
+  // row block 2 i + (w / 2) of the tile (the GEMM interleaves its wavefront rows)
+  const int r = (2 * i + (w >> 1)) * 32 + (lane & 31);
   if (r >= valid) return;
   constexpr size_t kTile = BM * BN / 4;
   const f32x4* src = reinterpret_cast<const f32x4*>(p.part) + (size_t)tt * sp.s * kTile +
