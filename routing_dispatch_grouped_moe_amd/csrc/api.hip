@@ -97,6 +97,8 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t f
   L.route_part = off;
   off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
   L.route_tickets = off; off = align256(off + (size_t)std::max(L.route_groups, 1) * 4);
+  L.route_logits = off;
+  if (route_tiled(S, E, dtype == MOE_BF16)) off = align256(off + (size_t)S * E * 4);
   // raw softmax gates only: token-slice partials of the dense dWg
   L.dwg_dense_part = off;
   if (!(flags & MOE_F_RENORM))
@@ -206,6 +208,13 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;
   launch_fill_i32(counts, 0, d->E, s);
+  if (route_tiled(d->S, d->E, bf16)) {
+    float* lg = logits ? logits : reinterpret_cast<float*>(w + L.route_logits);
+    launch_route_tiled(x, Wg, bias, lg, topk_idx, gates, counts,
+                       reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, L.epad, d->K,
+                       (d->flags & MOE_F_RENORM) != 0, s);
+    return launched();
+  }
   int32_t* tickets = reinterpret_cast<int32_t*>(w + L.route_tickets);
   launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, bf16, tickets, L.route_groups,
                       s);

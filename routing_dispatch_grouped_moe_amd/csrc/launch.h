@@ -44,6 +44,7 @@ struct WsLayout {
   size_t gemm_part;   // [tail_items, 256 * 256] fp32 K-split partial tiles of the last GEMM wave
   size_t route_part;  // [groups, route_parts, 32, epad] fp32 partial logits of a split router
   size_t route_tickets; // [groups] int32 parts finished per 32-token group
+  size_t route_logits;  // [S, E] fp32 logits of the tiled router when the caller keeps none
   size_t dwg_dense_part; // [splits, H, epad] fp32 token-slice partials of the dense dWg (raw gates)
   size_t total;
   int nb;             // dispatch blocks of 256 tokens
@@ -70,6 +71,13 @@ void launch_transpose_wg(const void* Wg, void* wgT, int H, int E, int epad, bool
                          bool blocked, int32_t* tickets, int ntickets, hipStream_t s);
 // K parts per 32-token group of the bf16 router (1: no split)
 int route_parts(int64_t S, int H, int epad);
+// many experts and tokens: the router as a tiled GEMM into fp32 logits (the
+// caller's, or the workspace's route_logits) plus a top-K launch; it reads Wg
+// in its [H][E] layout (no transposed copy)
+bool route_tiled(int64_t S, int E, bool bf16);
+void launch_route_tiled(const void* x, const void* Wg, const float* bias, float* logits,
+                        int32_t* idx, float* gates, int32_t* counts, uint32_t* status, int64_t S,
+                        int H, int E, int epad, int K, bool renorm, hipStream_t s);
 void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,
                   float* gates, int32_t* counts, uint32_t* status, int64_t S, int H, int E, int epad,
                   int K, bool renorm, bool bf16, int nparts, float* rpart, int32_t* tickets,

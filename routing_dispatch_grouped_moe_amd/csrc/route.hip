@@ -28,6 +28,7 @@
 #include "dev_common.h"
 #include "launch.h"
 #include "moe.h"
+#include "tile.h"
 
 namespace moe {
 
@@ -410,6 +411,186 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_mfma_kernel(const void
   // keys per lane: at most NCB (one wavefront row of K) or one (E < 64)
   route_tail<KS == 1 ? NCB : 1, kRouteWaves>(part, hist, KS, logits, idx, gates, counts, status,
                                              t0, nt, E, epad, K, renorm);
+}
+
+// ------------------------------------------------- tiled router (many E) --
+// With many experts and many tokens the fused router above streams the whole
+// router weight once per 32 tokens (at 384 experts and 8192 tokens, 256
+// blocks each reading 5.5 MB of weight through L2 into LDS: the L2 -> CU feed
+// bounds it).  Here the projection is a tiled GEMM instead: a block owns 128
+// tokens x 128 experts, so each weight byte is fed once per 128 tokens and
+// each activation byte once per 128 experts, and the logits go to memory
+// (fp32, bias added); a second launch then does the softmax, the top-K, the
+// gates and the counts per token from those logits.  The weight is read in
+// its [H][E] layout as a K-major tile (transposing LDS reads), so no
+// transposed copy is made.  Taken for bf16 with E >= 256 experts (a multiple
+// of 8: 16-byte rows) and at least 2048 tokens; the fused router keeps the
+// rest (few experts, or few tokens where it splits H over blocks).
+constexpr int kRgBM = 128, kRgBN = 128, kRgNS = 4;  // tile, LDS stages (3 in flight)
+
+bool route_tiled(int64_t S, int E, bool bf16) { return bf16 && E >= 256 && E % 8 == 0 && S >= 2048; }
+
+// logits [S, E] = x [S, H] * Wg [H, E] + bias; four wavefronts (2 x 2), each
+// 64 x 64 on v_mfma_f32_32x32x16_bf16 with the weight fragment as the first
+// operand (each lane ends with four consecutive experts of one token).
+__global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict__ x,
+                                                         const void* __restrict__ Wg,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ out, int S, int H,
+                                                         int E, int ntn) {
+  constexpr int kTileA = kRgBM * kBK * 2, kTileB = kRgBN * kBK * 2, kStage = kTileA + kTileB;
+  __shared__ __attribute__((aligned(1024))) char smem[kRgNS * kStage];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = bid / ntn, nt = bid - mt * ntn;
+  const int t0 = mt * kRgBM, e0 = nt * kRgBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int rows = min(kRgBM, S - t0);
+
+  // x rows of the tile (rows past S read zeros) and the weight columns
+  // e0 .. e0 + 127 (columns past E read other columns or zeros; they are
+  // never stored)
+  DmaOperand<true, kRgBM, 1, 4> da;
+  DmaOperand<false, kRgBN, 1, 4> db;
+  da.init(H, 0, w, lane);
+  db.init(E, 0, w, lane);
+  const uint16_t* const pa[1] = {reinterpret_cast<const uint16_t*>(x) + (int64_t)t0 * H};
+  const uint16_t* const pb[1] = {reinterpret_cast<const uint16_t*>(Wg) + e0};
+  const uint32_t a_bytes = (uint32_t)rows * (uint32_t)H * 2u;
+  const uint32_t b_bytes = ((uint32_t)H * (uint32_t)E - (uint32_t)e0) * 2u;
+  constexpr int kPA = DmaOperand<true, kRgBM, 1, 4>::kPer, kPB = DmaOperand<false, kRgBN, 1, 4>::kPer;
+  auto issue = [&](int kt, int st) {
+    u32x4 ra[1], rb[1];
+    da.rsrc_for(pa, a_bytes, H, kt * kBK, ra);
+    db.rsrc_for(pb, b_bytes, E, kt * kBK, rb);
+    char* sb = smem + st * kStage;
+#pragma unroll
+    for (int i = 0; i < kPA; ++i) da.issue_one(i, ra, sb, w);
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) db.issue_one(i, rb, sb + kTileA, w);
+  };
+  const int nk = H / kBK;
+#pragma unroll
+  for (int st = 0; st < kRgNS - 1; ++st) issue(st, st);  // past H: in-range reads, never used
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  uint32_t bbase[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bbase[j] = frag_km_base<kRgBN>(wn * 64 + j * 32, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wavefront's loads of step kt landed (those of the next NS - 2
+    // steps may still be in flight); after the barrier everyone's have, and
+    // every wavefront is done with step kt - 1's stage, which step
+    // kt + NS - 1 now refills
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRgNS - 2) * (kPA + kPB)) : "memory");
+    issue(kt + kRgNS - 1, (kt + kRgNS - 1) % kRgNS);
+    const char* sa = smem + (kt % kRgNS) * kStage;
+    const char* sbt = sa + kTileA;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      u32x4 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = frag_kc(sa, wm * 64 + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = frag_km_at<kRgBN>(sbt, bbase[j], kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0,
+              0, 0);
+    }
+  }
+  // no direct load may still be writing LDS when the block exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane l holds token row (l % 32) of each 32 x 32 block and experts
+  // 8 g + 4 (l / 32) + 0..3 (E is a multiple of 8, so a piece is all in or
+  // all out)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wm * 64 + i * 32 + (lane & 31);
+    if (r >= rows) continue;
+    float* orow = out + (int64_t)(t0 + r) * E;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = e0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+        if (c >= E) continue;
+        f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                   acc[i][j][4 * g + 3]};
+        if (bias != nullptr) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(bias + c);
+          v += b4;
+        }
+        *reinterpret_cast<f32x4*>(orow + c) = v;
+      }
+  }
+}
+
+// Softmax, top-K, gates and counts from the logit rows (the router GEMM's
+// output): 16 tokens per block, one per wavefront, their rows staged in LDS
+// and their (token, k) pairs counted in an LDS histogram.
+constexpr int kTopkTB = 16;
+
+template <int NJ>
+__global__ __launch_bounds__(64 * kTopkTB) void route_topk_kernel(
+    const float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gates,
+    int32_t* __restrict__ counts, uint32_t* __restrict__ status, int S, int E, int epad, int K,
+    int renorm) {
+  extern __shared__ __attribute__((aligned(16))) float rows_l[];  // [kTopkTB][epad]
+  __shared__ int hist[1024];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTopkTB;
+  const int nt = min(kTopkTB, S - t0);
+  for (int e = tid; e < E; e += 64 * kTopkTB) hist[e] = 0;
+  const int n4 = E / 4;
+  for (int i = tid; i < nt * n4; i += 64 * kTopkTB) {
+    const int t = i / n4, c = i - t * n4;
+    reinterpret_cast<f32x4*>(rows_l + t * epad)[c] =
+        reinterpret_cast<const f32x4*>(logits + (int64_t)(t0 + t) * E)[c];
+  }
+  __syncthreads();
+  route_tail<NJ, kTopkTB>(rows_l, hist, 1, nullptr, idx, gates, counts, status, t0, nt, E, epad,
+                          K, renorm);
+}
+
+void launch_route_tiled(const void* x, const void* Wg, const float* bias, float* logits,
+                        int32_t* idx, float* gates, int32_t* counts, uint32_t* status, int64_t S,
+                        int H, int E, int epad, int K, bool renorm, hipStream_t s) {
+  const int ntn = (E + kRgBN - 1) / kRgBN;
+  const int blocks = (int)((S + kRgBM - 1) / kRgBM) * ntn;
+  {
+    TimedLaunch tl("route", s);
+    hipLaunchKernelGGL(route_gemm_kernel, dim3(blocks), dim3(256), 0, s, x, Wg, bias, logits,
+                       (int)S, H, E, ntn);
+  }
+  const size_t lds = (size_t)kTopkTB * epad * sizeof(float);
+  const int tb = (int)((S + kTopkTB - 1) / kTopkTB);
+  TimedLaunch tl("route_topk", s);
+#define TOPK_CASE(NJ)                                                                          \
+  if ((E + 63) / 64 <= NJ) {                                                                   \
+    static bool attr = false;                                                                  \
+    if (!attr)                                                                                 \
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_topk_kernel<NJ>),         \
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) ==    \
+             hipSuccess;                                                                       \
+    hipLaunchKernelGGL(route_topk_kernel<NJ>, dim3(tb), dim3(64 * kTopkTB), lds, s, logits, idx, \
+                       gates, counts, status, (int)S, E, epad, K, renorm ? 1 : 0);            \
+    return;                                                                                    \
+  }
+  TOPK_CASE(4) TOPK_CASE(8) TOPK_CASE(16)
+#undef TOPK_CASE
 }
 
 // fp32 router: plain dot products, one (token, expert) pair per thread.

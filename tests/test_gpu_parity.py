@@ -113,6 +113,8 @@ CASES = [
     # 64-row tiles with a hot expert spanning several of them (ragged tail):
     # 400 rows over 16 experts, the Zipf-biased top expert takes most tokens
     ("c4_few_rows_hot_expert", "c4", dict(S=200, H=256, Hf=384, E=16, K=2, beta=4.0)),
+    # the tiled router (2048 tokens, 256 experts) inside the whole layer
+    ("c4_tiled_router", "c4", dict(S=2048, H=256, Hf=256, E=256, beta=1.0)),
     # the largest expert count and top-K the library accepts (1024 experts,
     # top-16; 2080 rows): spread over ~850 experts of at most ten rows each,
     # and Zipf-concentrated on ~28 experts with every token in the hottest

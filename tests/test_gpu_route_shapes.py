@@ -8,7 +8,9 @@ against the oracle's selection on the GPU's own fp32 logits (the integer
 decision taken in the same precision), gates to 1e-5 and per-expert counts
 bit for bit.  S = 100 leaves a ragged last block of 4 tokens.  A second test
 runs token counts on both sides of the H-split rule (split up to 1024 tokens);
-a third checks the load statistics of routing histograms (maxvio, load entropy).
+a third runs the tiled router (many experts and tokens: a tiled GEMM into fp32
+logits, then the top-K launch); a fourth checks the load statistics of
+routing histograms (maxvio, load entropy).
 """
 import sys
 
@@ -93,6 +95,45 @@ def test_route_split_boundary(S, H, E, K):
     assert_close("gates", to_host(gates), oracle.gate_weights(got_l, want_idx), F32_TOL)
     want_counts, _ = oracle.expert_counts(want_idx, E)
     np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
+
+
+# (S, H, E, K): the tiled router (at least 2048 tokens, at least 256 experts,
+# E a multiple of 8): one or several 128-expert tiles, a partial last tile,
+# ragged token tiles
+TILED = [(2048, 256, 256, 8), (2100, 512, 384, 8), (4000, 128, 1000, 16), (8192, 256, 384, 8),
+         (2049, 1024, 640, 4)]
+
+
+@pytest.mark.parametrize("S,H,E,K", TILED, ids=[f"S{s}_H{h}_E{e}_K{k}" for s, h, e, k in TILED])
+def test_route_tiled(S, H, E, K):
+    print(f"[route tiled] S={S} H={H} E={E} K={K}", flush=True)
+    sys.stdout.flush()
+    wl = make_workload("c3", S=S, H=H, Hf=128, E=E, K=K, host_weights=False)
+    d = L.dims(S, H, wl.Hf, E, K, "bf16")
+    ws = torch.zeros(L.moe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    x, Wg = to_dev(wl.x, "bf16"), to_dev(wl.Wg, "bf16")
+    bias = torch.from_numpy(wl.bias.astype(np.float32)).cuda()
+    logits = torch.empty(S, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
+    gates = torch.empty(S, K, dtype=torch.float32, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    L.moe_clear_status(ws)
+    L.moe_route(d, x, Wg, bias, logits, idx, gates, counts, ws)
+    # and once more with no logits buffer of the caller's (the workspace holds them)
+    idx2 = torch.empty_like(idx)
+    gates2 = torch.empty_like(gates)
+    counts2 = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    L.moe_route(d, x, Wg, bias, None, idx2, gates2, counts2, ws)
+    torch.cuda.synchronize()
+    assert L.moe_read_status(ws) == 0
+    got_l = to_host(logits)
+    assert_close("logits", got_l, oracle.router_logits(wl.x, wl.Wg, wl.bias), F32_TOL)
+    want_idx = oracle.topk_experts(got_l, K)
+    np.testing.assert_array_equal(to_host(idx), want_idx, err_msg="topk_idx")
+    assert_close("gates", to_host(gates), oracle.gate_weights(got_l, want_idx), F32_TOL)
+    want_counts, _ = oracle.expert_counts(want_idx, E)
+    np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
+    assert torch.equal(idx, idx2) and torch.equal(gates, gates2) and torch.equal(counts, counts2)
 
 
 def test_load_stats():
