@@ -93,6 +93,7 @@ struct GemmArgs {
   float* part;            // K-split partial tiles of the last wave (store epilogue)
   int tail_cap;           // capacity of part in tiles
   int ncu;                // compute units of the device (tiles in flight per wave)
+  int deal_whole;         // K-grouped with eorder: light experts go whole to one XCD
 };
 
 // ------------------------------------------------------------- epilogue --
@@ -194,34 +195,57 @@ __device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2,
   return true;
 }
 
-// K-grouped blocks go expert by expert (every XCD shares each expert's
-// tiles, so experts of different row counts load the XCDs evenly), the
-// experts in the tile table's longest-first order when one is given.  Inside
-// an expert the tiles run N fastest, or with PATCH each XCD takes a
-// contiguous range walked in groups of kGroupM M tiles x all N tiles (M
-// fastest), so the tiles an XCD holds at once form a compact patch whose
-// operand rows its L2 shares.  Measured: PATCH speeds up the few-row
-// dW1/dW3 product (-9% at 384 experts) and slows the others (dW2 there,
-// the many-row products), whose N-fastest order keeps each block's fp32
-// output rows contiguous.
+// K-grouped blocks go expert by expert, the experts in the tile table's
+// longest-first order when one is given.  With deal_whole, that order, and
+// tiles per expert a multiple of 8, the heavy experts' tiles are shared by
+// all XCDs (balanced load) and every other expert's tiles stay on one XCD
+// (one L2 fetch of its operand rows); otherwise every XCD shares every
+// expert.  Measured at 384 experts: whole dealing speeds dW2 up by 7-10% and
+// slows dW1/dW3 by 6-12%, so only dW2 asks for it.
+// Inside an expert's range the tiles run N fastest, or with PATCH in groups
+// of kGroupM M tiles x all N tiles (M fastest), so the tiles an XCD holds at
+// once form a compact patch whose operand rows its L2 shares.  Measured:
+// PATCH speeds up the few-row dW1/dW3 product (-9% at 384 experts) and slows
+// the others (dW2 there, the many-row products), whose N-fastest order keeps
+// each block's fp32 output rows contiguous.
 template <bool KGROUP, int BM, int BN, bool PATCH = false>
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int64_t& row0,
                                         int& valid, int& m0, int& n0) {
   if constexpr (KGROUP) {
     const int per_e = p.mtn * p.ntn;
-    const int slot = bid / per_e;
-    const int rem = bid - slot * per_e;
+    int slot, rp;
+    if (p.deal_whole && p.eorder != nullptr && (per_e & 7) == 0) {
+      // Block bid runs on XCD bid % 8 as that XCD's block bid / 8.  The first
+      // T experts of the dealing order (the heavy ones) are split eight ways,
+      // one contiguous eighth of each per XCD; every other expert goes whole
+      // to one XCD, dealt in snake order (0..7, 7..0, ...), so its operand
+      // rows are fetched into one L2 instead of eight.
+      const int x = bid & 7, j = bid >> 3, P = per_e >> 3;
+      int T = p.eorder[p.E];
+      if (T < 0 || T > p.E || ((p.E - T) & 7)) T = p.E;
+      if (j < T * P) {
+        slot = j / P;
+        rp = x * P + (j - slot * P);
+      } else {
+        const int jc = j - T * P, wv = jc / per_e;
+        rp = jc - wv * per_e;
+        slot = T + 8 * wv + ((wv & 1) ? 7 - x : x);
+      }
+    } else {
+      slot = bid / per_e;
+      const int rem = bid - slot * per_e;
+      rp = PATCH ? xcd_remap(rem, per_e) : rem;
+    }
     e = p.eorder ? p.eorder[slot] : slot;
     if constexpr (PATCH) {
-      const int rp = xcd_remap(rem, per_e);
       const int per_group = kGroupM * p.ntn;
       const int g = rp / per_group, r = rp - g * per_group;
       const int gm = min(kGroupM, p.mtn - g * kGroupM);  // the last group may be short
       m0 = (g * kGroupM + r % gm) * BM;
       n0 = (r / gm) * BN;
     } else {
-      m0 = (rem / p.ntn) * BM;
-      n0 = (rem % p.ntn) * BN;
+      m0 = (rp / p.ntn) * BM;
+      n0 = (rp % p.ntn) * BN;
     }
     row0 = p.cu[e];
     valid = max(0, p.cu[e + 1] - p.cu[e]);
@@ -1300,6 +1324,14 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     }
     eorder[rank] = e;
   }
+  if (eorder != nullptr) {
+    // T: experts with more than twice the mean row count, rounded up so that
+    // E - T is a multiple of 8 (the weight-gradient products split these
+    // eight ways across the XCDs and deal the rest whole)
+    const int64_t rows = E > 0 ? (int64_t)cu[E] - cu[0] : 0;
+    const int hot = __syncthreads_count(e < E && (int64_t)c * E > 2 * rows);
+    if (e == 0) eorder[E] = hot + ((E - hot) & 7);
+  }
 }
 
 void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, bool expert_order,
@@ -1483,6 +1515,7 @@ void launch_bwd_dw2(const void* a, const void* dy, const int32_t* cu, const int3
   // dW2[e][Hf, H] = a[rows, Hf]^T * dy[rows, H]
   GemmArgs p{};
   p.cu = cu; p.eorder = eorder; p.E = E; p.M = Hf; p.N = H;
+  p.deal_whole = 1;  // light experts whole per XCD (-7..10% at 384 experts)
   p.A0 = a; p.lda = Hf;
   p.B0 = dy; p.ldb = H;
   p.C0 = dW2; p.ldc = H; p.sCe = (int64_t)Hf * H;
@@ -1502,6 +1535,7 @@ void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int
   // dW1[e][H, Hf] = xd[rows, H]^T * dh1[rows, Hf]; dW3 likewise with dh3.
   GemmArgs p{};
   p.cu = cu; p.eorder = eorder; p.E = E; p.M = H; p.N = Hf;
+  p.deal_whole = 0;  // all XCDs share each expert (whole per XCD: +6..12% at 384 experts)
   p.A0 = xd; p.lda = H;
   p.B0 = dh1; p.B1 = dh3; p.ldb = Hf;
   p.C0 = dW1; p.C1 = dW3; p.ldc = Hf; p.sCe = (int64_t)H * Hf;

@@ -36,7 +36,8 @@ struct WsLayout {
   size_t base;        // dispatch: [nb, E] int32 first row of each (block, expert)
   size_t tiles;       // grouped GEMM: [max_tiles] int2 (expert, first row) per M tile
   size_t ntiles;      // int32 number of valid M tiles
-  size_t eorder;      // [E] int32 experts by descending row count (ties: lower index first)
+  size_t eorder;      // [E + 1] int32 experts by descending row count (ties: lower index
+                      // first), then the count of them the weight gradients split by XCD
   size_t dl_row;      // [R] fp32 dlogit of each dispatched row
   size_t dwg_items;   // [dwg_max_items] int4 (expert, first row, rows, 0) row items of dWg
   size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
