@@ -119,8 +119,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         for (int i = 0; i < PC::kEl; ++i) acc[i] += g[k] * v[i];
       }
       if (p < pieces)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
-                                  ((int64_t)s * H + (int64_t)p * PC::kEl) * PC::kEb) = PC::pack(acc);
+        __builtin_nontemporal_store(  // non-temporal: -7% at 384 experts
+            PC::pack(acc), reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
+                                                    ((int64_t)s * H + (int64_t)p * PC::kEl) * PC::kEb));
     }
   }
 }

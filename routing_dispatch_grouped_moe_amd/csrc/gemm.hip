@@ -906,7 +906,13 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
       for (int it = 0; it < NR / kPass; ++it) {
         const int qd = it * kPass, rd = qd + (qd / SEG) * GAP;
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + qd * RS + ((uint32_t)(c ^ ((q0 + qd) & 15)) << 4));
-        if (rd < left) *reinterpret_cast<u32x4*>(dst + (int64_t)rd * p.ldc) = v;
+        if (rd < left) {
+          // non-temporal, except the forward SwiGLU outputs, which the next
+          // product reads at once (measured: down, dA -5%; up +2.5% if NT)
+          u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)rd * p.ldc);
+          if constexpr (EPI == EPI_SWIGLU_FWD) *d = v;
+          else __builtin_nontemporal_store(v, d);
+        }
       }
     };
     using R128 = std::integral_constant<int, 128>;
