@@ -99,9 +99,9 @@ def test_route_split_boundary(S, H, E, K):
 
 # (S, H, E, K): the tiled router (at least 2048 tokens, at least 256 experts,
 # E a multiple of 8): one or several 128-expert tiles, a partial last tile,
-# ragged token tiles
+# ragged token tiles, and (32768 tokens) three blocks per compute unit
 TILED = [(2048, 256, 256, 8), (2100, 512, 384, 8), (4000, 128, 1000, 16), (8192, 256, 384, 8),
-         (2049, 1024, 640, 4)]
+         (2049, 1024, 640, 4), (32768, 128, 384, 8)]
 
 
 @pytest.mark.parametrize("S,H,E,K", TILED, ids=[f"S{s}_H{h}_E{e}_K{k}" for s, h, e, k in TILED])
