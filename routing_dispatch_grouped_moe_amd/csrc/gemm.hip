@@ -128,12 +128,29 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 // Tile coordinates of a block.  Returns false when the block has no tile.
 // valid: rows of the tile inside the expert (M-grouped) or the expert's row
 // count, i.e. the reduction length (K-grouped).
+//
+// M tile groups (kGroupM M tiles x all N tiles) in the order the XCDs take
+// them: XCD a walks a contiguous range of positions pg = a Q + b (Q = G / 8
+// groups each), which deals it group 8 b + a for even b and 8 b + 7 - a for
+// odd b (snake order); the last G mod 8 groups keep their place.  The tile
+// table lists the M tiles longest expert first, so the XCDs start on the
+// costly full tiles of the heavy experts together and end on the short
+// ones, with like work each.
+__device__ __forceinline__ int group_dealt(int pg, int G) {
+  const int Q = G >> 3;
+  if (pg >= 8 * Q) return pg;
+  const int a = pg / Q, b = pg - a * Q;
+  return 8 * b + ((b & 1) ? 7 - a : a);
+}
+
 // M-grouped tile t of T = ntiles * ntn: groups of kGroupM M tiles (fewer in
-// the last group) walked with the M tile fastest.
+// the last group) walked with the M tile fastest, full groups dealt to the
+// XCDs by group_dealt.
 __device__ __forceinline__ void mtile_of(int t, int ntiles, int ntn, int& mt, int& nt) {
   const int per_group = kGroupM * ntn, g4 = ntiles / kGroupM * per_group;
   if (t < g4) {
-    const int g = t / per_group, r = t - g * per_group;
+    const int pg = t / per_group, r = t - pg * per_group;
+    const int g = group_dealt(pg, ntiles / kGroupM);
     mt = g * kGroupM + r % kGroupM;
     nt = r / kGroupM;
   } else {
@@ -258,8 +275,8 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
     const int nvalid = (*p.ntiles + kGroupM - 1) / kGroupM * per_group;
     if (bid >= nvalid) return false;
     bid = xcd_remap(bid, nvalid);
-    const int g = bid / per_group, r = bid - g * per_group;
-    const int mt = g * kGroupM + r % kGroupM;
+    const int pg = bid / per_group, r = bid - pg * per_group;
+    const int mt = group_dealt(pg, nvalid / per_group) * kGroupM + r % kGroupM;
     n0 = (r / kGroupM) * BN;
     if (mt >= *p.ntiles) return false;
     const int2 t = p.tiles[mt];
@@ -1288,10 +1305,11 @@ __device__ int block_exclusive_scan_1024_g(int v, int* sh, int* total) {
   return incl - v;
 }
 
-// M tiles of every expert (M-grouped products) and, when eorder is given,
-// the order in which the K-grouped products deal out experts: by descending
-// row count, ties to the lower index.  A K-grouped tile's K loop runs over its expert's rows, so
-// under skew the hot expert's tiles are the long ones; dealt first, they
+// The experts by descending row count (ties to the lower index): the M
+// tiles of the M-grouped products are listed expert by expert in that
+// order, and when eorder is given it is also the order in which the
+// K-grouped products deal out experts.  Under skew the hot experts' tiles
+// are the costly ones (full M tiles; long K loops); taken first, they
 // overlap the many short tiles instead of trailing after them.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ cu, int E,
                                                           int bm, int max_tiles,
@@ -1300,20 +1318,21 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ eorder) {
   __shared__ int sh[1024];
   __shared__ __attribute__((aligned(16))) int cnt[1024];
+  __shared__ int nt_at[1024];     // M tiles of the expert at each rank
+  __shared__ int start_at[1024];  // its first slot in the table
   const int e = threadIdx.x;
   // A malformed cu (not monotone) yields no tiles for that expert rather than
   // a table overflow.
   const int c = e < E ? max(0, cu[e + 1] - cu[e]) : 0;
   cnt[e] = e < E ? c : -1;  // past E: ranks below every expert
   const int nt = (c + bm - 1) / bm;
-  int total;
-  const int start = block_exclusive_scan_1024_g(nt, sh, &total);  // its barriers publish cnt
-  for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
-  if (e == 0) *ntiles = min(total, max_tiles);
-  if (eorder != nullptr && e < E) {
-    // rank = experts ahead of e; counts read four at a time (every thread
-    // reads the same words: broadcast), four reads in flight per iteration
-    int rank = 0;
+  if (e >= E) nt_at[e] = 0;  // the ranks of the experts are exactly 0 .. E-1
+  __syncthreads();
+  // rank = experts ahead of e (more rows, or as many and a lower index);
+  // counts read four at a time (every thread reads the same words:
+  // broadcast), four reads in flight per iteration
+  int rank = 0;
+  if (e < E) {
     const int4* c4 = reinterpret_cast<const int4*>(cnt);
     for (int j4 = 0; j4 < (E + 15) / 16 * 4; j4 += 4) {
       int4 v[4];
@@ -1328,8 +1347,19 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
         rank += (v[u].w > c || (v[u].w == c && j + 3 < e)) ? 1 : 0;
       }
     }
-    eorder[rank] = e;
+    nt_at[rank] = nt;
+    if (eorder != nullptr) eorder[rank] = e;
   }
+  __syncthreads();
+  // M tiles listed expert by expert in that order (thread r scans rank r)
+  int total;
+  start_at[e] = block_exclusive_scan_1024_g(nt_at[e], sh, &total);
+  __syncthreads();
+  if (e < E) {
+    const int start = start_at[rank];
+    for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
+  }
+  if (e == 0) *ntiles = min(total, max_tiles);
   if (eorder != nullptr) {
     // T: experts with more than twice the mean row count, rounded up so that
     // E - T is a multiple of 8 (the weight-gradient products split these
