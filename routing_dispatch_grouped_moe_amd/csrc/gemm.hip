@@ -130,17 +130,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 // count, i.e. the reduction length (K-grouped).
 //
 // M tile groups (kGroupM M tiles x all N tiles) in the order the XCDs take
-// them: XCD a walks a contiguous range of positions pg = a Q + b (Q = G / 8
-// groups each), which deals it group 8 b + a for even b and 8 b + 7 - a for
-// odd b (snake order); the last G mod 8 groups keep their place.  The tile
-// table lists the M tiles longest expert first, so the XCDs start on the
-// costly full tiles of the heavy experts together and end on the short
-// ones, with like work each.
+// them.  The tile table lists the M tiles longest expert first, so groups
+// come in falling cost: under skew the first are the heavy experts' full
+// tiles (MFMA-bound), the last the light experts' short ones (bound by the
+// weight stream).  XCD a walks a contiguous range of positions pg = a Q + b
+// (Q = G / 8 groups each).  Its i-th costliest share is group 8 i + a for
+// even i and 8 i + 7 - a for odd i (snake order: like work per XCD), and it
+// takes its shares alternately from the costly and the cheap end, the even
+// XCDs starting at the costly end and the odd ones at the cheap end, so
+// that at any time about half the XCDs run MFMA-bound tiles while the rest
+// stream weights.  The last G mod 8 groups keep their place.
 __device__ __forceinline__ int group_dealt(int pg, int G) {
   const int Q = G >> 3;
   if (pg >= 8 * Q) return pg;
-  const int a = pg / Q, b = pg - a * Q;
-  return 8 * b + ((b & 1) ? 7 - a : a);
+  const int a = pg / Q, b = pg - a * Q, h = b >> 1;
+  const int i = (((b ^ a) & 1) == 0) ? h : Q - 1 - h;
+  return 8 * i + ((i & 1) ? 7 - a : a);
 }
 
 // M-grouped tile t of T = ntiles * ntn: groups of kGroupM M tiles (fewer in
