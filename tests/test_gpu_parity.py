@@ -115,6 +115,13 @@ CASES = [
     ("c4_few_rows_hot_expert", "c4", dict(S=200, H=256, Hf=384, E=16, K=2, beta=4.0)),
     # the tiled router (2048 tokens, 256 experts) inside the whole layer
     ("c4_tiled_router", "c4", dict(S=2048, H=256, Hf=256, E=256, beta=1.0)),
+    # dW2's XCD dealing with 8 tiles per expert and 12 experts (not a
+    # multiple of 8): the two heavy experts (more than twice the mean rows)
+    # plus two more split eight ways, the other eight whole, one per XCD,
+    # some of them empty; few rows (eight-wavefront tiles) and many rows
+    # (one wavefront per SIMD)
+    ("c4_dw2_dealing_few_rows", "c4", dict(S=1000, H=1024, Hf=512, E=12, K=2, beta=2.0)),
+    ("c4_dw2_dealing_many_rows", "c4", dict(S=4096, H=1024, Hf=512, E=12, K=2, beta=2.0)),
     # the largest expert count and top-K the library accepts (1024 experts,
     # top-16; 2080 rows): spread over ~850 experts of at most ten rows each,
     # and Zipf-concentrated on ~28 experts with every token in the hottest
