@@ -56,84 +56,89 @@ __global__ __launch_bounds__(256) void dispatch_bits_kernel(const int32_t* __res
   }
 }
 
-// Exclusive scan of up to 1024 ints held one per thread (blockDim.x == 1024).
-__device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int add = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
   }
-  const int incl = sh[tid];
-  *total = sh[1023];
-  __syncthreads();
-  return incl - v;
+  return v;
 }
 
 // Counts of every (block, expert) -> cu_seqlens and the first row of every
-// (block, expert) run.  With the whole [nb][E] count table in LDS (it is
-// loaded in one round of independent coalesced loads, eight per thread in
-// flight), thread e scans its expert's column there, a block scan over the
-// experts gives cu, and the bases leave as coalesced rows.  Tables larger
-// than the LDS budget take the per-thread column walk through global memory.
+// (block, expert) run.  The [nb][E] count table is staged in LDS with its
+// loads all in flight at once (up to sixteen per thread); thread e then
+// scans its expert's column there, the expert totals are scanned with lane
+// shuffles (per wavefront, then across the sixteen wavefront sums), and the
+// bases leave as coalesced rows.  Tables larger than the LDS budget take the
+// per-thread column walk through global memory.
 constexpr int kScanLdsInts = 32768;  // 128 KB of dynamic LDS
+constexpr int kScanLoads = 16;       // table loads in flight per thread
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
                                                              int32_t* __restrict__ base,
                                                              int32_t* __restrict__ cu, int nb,
                                                              int E) {
   extern __shared__ int tab[];  // [nb][E] when it fits
-  __shared__ int sh[1024];
   __shared__ int start_e[1024];
-  const int e = threadIdx.x;
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool in_lds = (int64_t)nb * E <= kScanLdsInts;
   const int n = in_lds ? nb * E : 0;
   int tot = 0;
   if (in_lds) {
-    for (int i0 = 0; i0 < n; i0 += 8 * 1024) {
-      int v[8];
+    for (int i0 = 0; i0 < n; i0 += kScanLoads * 1024) {
+      int v[kScanLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 1024 + e;
+      for (int u = 0; u < kScanLoads; ++u) {
+        const int i = i0 + u * 1024 + tid;
         v[u] = i < n ? hist[i] : 0;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 1024 + e;
+      for (int u = 0; u < kScanLoads; ++u) {
+        const int i = i0 + u * 1024 + tid;
         if (i < n) tab[i] = v[u];
       }
     }
     __syncthreads();
-    if (e < E) {
+    if (tid < E) {
       // exclusive prefix of the column, in place
       for (int b = 0; b < nb; ++b) {
-        const int c = tab[b * E + e];
-        tab[b * E + e] = tot;
+        const int c = tab[b * E + tid];
+        tab[b * E + tid] = tot;
         tot += c;
       }
     }
-  } else if (e < E) {
+  } else if (tid < E) {
     for (int b = 0; b < nb; ++b) {
-      const int c = hist[(size_t)b * E + e];
-      base[(size_t)b * E + e] = tot;
+      const int c = hist[(size_t)b * E + tid];
+      base[(size_t)b * E + tid] = tot;
       tot += c;
     }
   }
-  int all;
-  const int start = block_exclusive_scan_1024(e < E ? tot : 0, sh, &all);  // its barriers publish tab
-  if (e < E) {
-    cu[e] = start;
-    start_e[e] = start;
+  // exclusive prefix of the expert totals: per wavefront, then across them
+  const int incl = wave_incl_scan(tid < E ? tot : 0);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();  // also publishes the scanned columns
+  if (w == 0) {
+    const int s16 = lane < 16 ? wsum[lane] : 0;
+    const int i16 = wave_incl_scan(s16);
+    if (lane < 16) wsum[lane] = i16 - s16;
   }
-  if (e == 0) cu[E] = all;
+  __syncthreads();
+  const int start = wsum[w] + incl - (tid < E ? tot : 0);
+  if (tid < E) {
+    cu[tid] = start;
+    start_e[tid] = start;
+  }
+  if (tid == E - 1) cu[E] = start + tot;
   __syncthreads();
   if (in_lds) {
-    for (int i = e; i < n; i += 1024) base[i] = tab[i] + start_e[i % E];
-  } else if (e < E) {
-    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += start;
+    for (int i = tid; i < n; i += 1024) base[i] = tab[i] + start_e[i % E];
+  } else if (tid < E) {
+    for (int b = 0; b < nb; ++b) base[(size_t)b * E + tid] += start;
   }
 }
 

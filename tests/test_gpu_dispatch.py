@@ -5,9 +5,9 @@ guide: every (token, k) pair gets a row, experts' rows contiguous, cu_seqlens
 the offsets; rows of one expert in ascending token order), so the oracle's
 counting sort fixes every integer output and xd is an exact copy.  The cases
 cover the count-table scan in both of its forms (the [blocks][experts] table
-staged in LDS, and the larger tables that take the per-expert walk through
-global memory), ragged token counts, empty experts and one expert taking
-every pair.
+staged in LDS, in one or more rounds of loads, and the larger tables that
+take the per-expert walk through global memory), the LDS budget's boundary,
+ragged token counts, empty experts and one expert taking every pair.
 """
 import sys
 
@@ -63,6 +63,7 @@ CASES = [
     (32768, 128, 1024, 1, None),   # 128 x 1024 = 131072: global-memory walk
     (8193, 128, 1024, 4, None),    # 33 x 1024 = 33792: just past the LDS table
     (8192, 128, 1024, 4, None),    # 32 x 1024 = 32768: exactly the LDS table
+    (20000, 128, 256, 2, None),    # 79 x 256: LDS, more than one round of loads
     (70, 128, 1000, 16, None),     # most experts empty
 ]
 
