@@ -430,10 +430,12 @@ constexpr int kRgBM = 128, kRgBN = 128, kRgNS = 4;  // tile, LDS stages (3 in fl
 
 bool route_tiled(int64_t S, int E, bool bf16) { return bf16 && E >= 256 && E % 8 == 0 && S >= 2048; }
 
-// logits [S, E] = x [S, H] * Wg [H, E] + bias; four wavefronts (2 x 2), each
-// 64 x 64 on v_mfma_f32_32x32x16_bf16 with the weight fragment as the first
-// operand (each lane ends with four consecutive experts of one token).
-__global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict__ x,
+// logits [S, E] = x [S, H] * Wg [H, E] + bias; kRgWaves wavefronts (2 along
+// the tokens), each 64 tokens x 128 / (kRgWaves / 2) experts on
+// v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand
+// (each lane ends with four consecutive experts of one token).
+constexpr int kRgWaves = 8;
+__global__ __launch_bounds__(64 * kRgWaves) void route_gemm_kernel(const void* __restrict__ x,
                                                          const void* __restrict__ Wg,
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ out, int S, int H,
@@ -445,21 +447,23 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict_
   const int t0 = mt * kRgBM, e0 = nt * kRgBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  constexpr int kWN = kRgWaves / 2, kWNT = kRgBN / kWN, NJ = kWNT / 32;
+  const int wm = w / kWN, wn = w % kWN;
   const int rows = min(kRgBM, S - t0);
 
   // x rows of the tile (rows past S read zeros) and the weight columns
   // e0 .. e0 + 127 (columns past E read other columns or zeros; they are
   // never stored)
-  DmaOperand<true, kRgBM, 1, 4> da;
-  DmaOperand<false, kRgBN, 1, 4> db;
+  DmaOperand<true, kRgBM, 1, kRgWaves> da;
+  DmaOperand<false, kRgBN, 1, kRgWaves> db;
   da.init(H, 0, w, lane);
   db.init(E, 0, w, lane);
   const uint16_t* const pa[1] = {reinterpret_cast<const uint16_t*>(x) + (int64_t)t0 * H};
   const uint16_t* const pb[1] = {reinterpret_cast<const uint16_t*>(Wg) + e0};
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)H * 2u;
   const uint32_t b_bytes = ((uint32_t)H * (uint32_t)E - (uint32_t)e0) * 2u;
-  constexpr int kPA = DmaOperand<true, kRgBM, 1, 4>::kPer, kPB = DmaOperand<false, kRgBN, 1, 4>::kPer;
+  constexpr int kPA = DmaOperand<true, kRgBM, 1, kRgWaves>::kPer;
+  constexpr int kPB = DmaOperand<false, kRgBN, 1, kRgWaves>::kPer;
   auto issue = [&](int kt, int st) {
     u32x4 ra[1], rb[1];
     da.rsrc_for(pa, a_bytes, H, kt * kBK, ra);
@@ -474,16 +478,16 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict_
 #pragma unroll
   for (int st = 0; st < kRgNS - 1; ++st) issue(st, st);  // past H: in-range reads, never used
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  uint32_t bbase[2];
+  uint32_t bbase[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) bbase[j] = frag_km_base<kRgBN>(wn * 64 + j * 32, lane);
+  for (int j = 0; j < NJ; ++j) bbase[j] = frag_km_base<kRgBN>(wn * kWNT + j * 32, lane);
 
   for (int kt = 0; kt < nk; ++kt) {
     // this wavefront's loads of step kt landed (those of the next NS - 2
@@ -496,15 +500,15 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict_
     const char* sbt = sa + kTileA;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      u32x4 af[2], bf[2];
+      u32x4 af[2], bf[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) af[i] = frag_kc(sa, wm * 64 + i * 32, kk, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = frag_km_at<kRgBN>(sbt, bbase[j], kk);
+      for (int j = 0; j < NJ; ++j) bf[j] = frag_km_at<kRgBN>(sbt, bbase[j], kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0,
               0, 0);
@@ -522,10 +526,10 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const void* __restrict_
     if (r >= rows) continue;
     float* orow = out + (int64_t)(t0 + r) * E;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = e0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+        const int c = e0 + wn * kWNT + j * 32 + 8 * g + 4 * (lane >> 5);
         if (c >= E) continue;
         f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                    acc[i][j][4 * g + 3]};
@@ -572,7 +576,7 @@ void launch_route_tiled(const void* x, const void* Wg, const float* bias, float*
   const int blocks = (int)((S + kRgBM - 1) / kRgBM) * ntn;
   {
     TimedLaunch tl("route", s);
-    hipLaunchKernelGGL(route_gemm_kernel, dim3(blocks), dim3(256), 0, s, x, Wg, bias, logits,
+    hipLaunchKernelGGL(route_gemm_kernel, dim3(blocks), dim3(64 * kRgWaves), 0, s, x, Wg, bias, logits,
                        (int)S, H, E, ntn);
   }
   const size_t lds = (size_t)kTopkTB * epad * sizeof(float);
