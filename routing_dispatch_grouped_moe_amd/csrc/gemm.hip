@@ -343,8 +343,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
+// Largest row count r (BM / 2^j, at least 32) whose r rows of rf bytes fit
+// in lds bytes: the fp32 epilogue's staging rounds.
+constexpr int f32_stage_rows(int lds, int rf, int bm) {
+  return (bm > 32 && bm * rf > lds) ? f32_stage_rows(lds, rf, bm / 2) : bm;
+}
+
+// NS: LDS operand stages.  NS == 2 double-buffers the K loop (one block per
+// CU); NS == 1 keeps one stage, which the next K step's staged registers
+// overwrite after a barrier, so that two blocks share a CU (four wavefronts
+// per SIMD, at most 128 registers each) and one block's fp32 stores can
+// overlap the other's loads and MFMAs.  For that the two must not run in
+// step: the first-round blocks that take the second slot of each CU (block
+// ids ncu .. 2 ncu - 1, as blocks are handed to every CU once before any
+// gets a second) start about 8 us late, roughly half a few-row tile's life,
+// and the blocks that replace them inherit the offset.  Measured at 384
+// experts: dW1/dW3 10.2 ms with both in step, 9.6-9.7 ms with the offset.
+template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI,
+          int NS = 2>
+__global__ __launch_bounds__(kThreads, NS == 1 ? 4 : 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int kWaves = kThreads / 64;
   constexpr int WM = BM / 2, WN = BN / 4;      // wavefront tile (per B operand)
@@ -483,12 +500,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   sa.store(smem, tid);
   sb.store(smem + kTileA, tid);
   lds_barrier();
+  if constexpr (NS == 1) {
+    if ((int)blockIdx.x >= p.ncu && (int)blockIdx.x < 2 * p.ncu) {
+      __builtin_amdgcn_s_sleep(127);  // 64 x 127 clocks each
+      __builtin_amdgcn_s_sleep(127);
+    }
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * kStage;
-    char* nxt = smem + ((kt + 1) & 1) * kStage;
+    char* cur = NS == 2 ? smem + (kt & 1) * kStage : smem;
+    char* nxt = NS == 2 ? smem + ((kt + 1) & 1) * kStage : smem;
     if (kt + 1 < nk) load(kt + 1);
     compute(cur);
     if (kt + 1 < nk) {
+      if constexpr (NS == 1) lds_barrier();  // every wavefront is done reading the stage
       sa.store(nxt, tid);
       sb.store(nxt + kTileA, tid);
     }
@@ -496,13 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   }
 
   if constexpr (EPI == EPI_F32) {
-    // fp32 weight gradient of expert e: the 2 x kStage bytes of LDS (free
+    // fp32 weight gradient of expert e: the NS x kStage bytes of LDS (free
     // after the loop's last barrier) hold kRows rows of BN floats (RF bytes,
     // 16-byte chunk c of row q at c ^ (q & 15)); non-temporal whole-row
     // stores.  Each operand's BM rows go in BM / kRows rounds; a wavefront
     // stages the 32-row blocks of its rows that fall in the round.
     constexpr int RF = BN * 4, LPRF = BN / 4, RPIF = 64 / LPRF;
-    constexpr int kRows = (2 * kStage / RF) < BM ? (2 * kStage / RF) : BM;
+    constexpr int kRows = f32_stage_rows(NS * kStage, RF, BM);
     constexpr int kRoundsPerOp = BM / kRows;
     static_assert(kRows % 32 == 0 && BM % kRows == 0 && kRows % (kWaves * RPIF) == 0,
                   "fp32 staging rounds");
@@ -1385,7 +1409,7 @@ void launch_tile_table(const int32_t* cu, int E, const WsLayout& L, char* ws, bo
 
 // -------------------------------------------------------------- launches --
 template <int BM, int BN, bool A_KC, bool B_KC, bool DUAL, bool TWOSEG, bool KGROUP, int EPI,
-          bool W4 = true>
+          bool W4 = true, int NS = 2>
 static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16, hipStream_t s) {
   static_assert(KGROUP || BM == kGemmBM || (BM == kGemmBMFew && !W4),
                 "M-grouped tiles follow the tile table");
@@ -1408,7 +1432,7 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
   if (blocks <= 0) return;
   TimedLaunch tl(name, s);
   if (bf16) {
-    constexpr int lds = 2 * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
+    constexpr int lds = NS * (BM * kBK * 2 + (DUAL ? 2 : 1) * BN * kBK * 2);
     static bool attr = false;
     if constexpr (W4 && EPI != EPI_F32_ACC) {
       // the one-wavefront-per-SIMD form; accumulating weight gradients keep
@@ -1423,7 +1447,7 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
                              dim3(256), 0, s, p);
       }
     } else {
-      auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI>;
+      auto kern = gemm_bf16_kernel<BM, BN, A_KC, B_KC, DUAL, TWOSEG, KGROUP, EPI, NS>;
       // a failure stays the thread's last HIP error (so the entry point
       // reports it) and the next call tries again
       if (!attr)
@@ -1586,8 +1610,15 @@ void launch_bwd_dw13(const void* xd, const void* dh1, const void* dh3, const int
                                                                                bf16, s);
   else if (many_rows(R, E))
     gemm_launch<256, 128, false, false, true, false, true, EPI_F32, true>("bwd_dW13", p, 0, bf16, s);
-  else
+  else if (bf16) {
+    // few rows: 128 x 128 tiles, two blocks per CU (measured at 384 experts:
+    // 10.2-11.0 -> 9.6-10.0 ms against 256 x 128 tiles, one block per CU)
+    p.ncu = device_cus();
+    gemm_launch<128, 128, false, false, true, false, true, EPI_F32, false, 1>("bwd_dW13", p, 0,
+                                                                            bf16, s);
+  } else {
     gemm_launch<256, 128, false, false, true, false, true, EPI_F32, false>("bwd_dW13", p, 0, bf16, s);
+  }
 }
 
 }  // namespace moe
