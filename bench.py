@@ -221,6 +221,9 @@ def main():
                     help="also time the step captured in one HIP graph (graph_ms_per_step)")
     ap.add_argument("--recompute", action="store_true",
                     help="keep no h1/h3 between forward and backward (the backward recomputes them)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="instead of the layer, time the vendor BLAS (torch.bmm, hipBLASLt) on the "
+                         "workload's per-expert products at balanced load, for comparison")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB read + 512 MiB write kernel first (a known-size kernel "
                          "for scaling HBM traffic counters)")
@@ -239,6 +242,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.library_gemm:
+        library_gemm(args.config)
+        return
     wl = make_workload(args.config, maxvio=args.maxvio, host_weights=False)
     cfg = wl.cfg
     bf16 = wl.dtype == "bf16"
@@ -564,6 +570,59 @@ def main():
                   f"  {v.get('bound', ''):5s} {100 * v.get('frac', 0):6.1f}%", file=sys.stderr)
         for k, v in calls_ms.items():
             print(f"  call {k:19s} {v * 1e3:10.1f} us", file=sys.stderr)
+
+
+def library_gemm(config):
+    """Vendor BLAS (torch.bmm, i.e. hipBLASLt) on the workload's expert products.
+
+    Every expert gets the balanced row count S*K/E; one projection each of
+    the up and down products and the weight-gradient shape (bf16 output,
+    where the layer writes fp32).  Contiguous operands only.  Prints one
+    JSON line; a comparison point, not part of the layer.
+    """
+    import torch
+    from synth import CONFIGS
+    cfg = CONFIGS[config]
+    if cfg.get("dtype") != "bf16":
+        print(json.dumps({"library_gemm": None, "reason": "bf16 workloads only"}))
+        return
+    S, E, K, H, Hf = cfg["S"], cfg["E"], cfg["K"], cfg["H"], cfg["Hf"]
+    r = max(1, S * K // E)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    bf = torch.bfloat16
+
+    def rnd(*shape):
+        return (torch.randn(*shape, device=dev, generator=g) * 0.05).to(bf)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    res = {}
+    flops = 2 * E * r * H * Hf
+    for name, (ashape, bshape, oshape) in {
+            "up_one_projection": ((E, r, H), (E, H, Hf), (E, r, Hf)),
+            "down": ((E, r, Hf), (E, Hf, H), (E, r, H)),
+            "weight_grad_shape_bf16_out": ((E, H, r), (E, r, Hf), (E, H, Hf))}.items():
+        A, B = rnd(*ashape), rnd(*bshape)
+        us = timed(lambda: torch.bmm(A, B), 10)
+        byts = 2 * (A.numel() + B.numel() + oshape[0] * oshape[1] * oshape[2])
+        res[name] = {"shape": f"bmm {list(ashape)} x {list(bshape)}", "us": round(us, 1),
+                     "tflops": round(flops / us / 1e6, 1), "mfma_frac": round(flops / us / 1e6 / 2500, 3),
+                     "gb": round(byts / 1e9, 3), "tbs": round(byts / us / 1e6, 2)}
+        del A, B
+        torch.cuda.empty_cache()
+    print(json.dumps({"library_gemm": res, "workload": cfg["workload"], "rows_per_expert": r}),
+          flush=True)
 
 
 def parse_clock(data):
