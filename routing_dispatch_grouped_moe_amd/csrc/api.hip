@@ -81,7 +81,7 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t f
   L.hist = off; off = align256(off + (size_t)L.nb * E * 4);
   L.base = off; off = align256(off + (size_t)L.nb * E * 4);
   L.tiles = off; off = align256(off + (size_t)std::max(L.max_tiles, 1) * 8);
-  L.ntiles = off; off = align256(off + 4);
+  L.ntiles = off; off = align256(off + 8);
   L.eorder = off; off = align256(off + (size_t)(E + 1) * 4);
   L.dl_row = off; off = align256(off + (size_t)std::max<int64_t>(R, 1) * 4);
   L.dwg_items = off; off = align256(off + (size_t)std::max(L.dwg_max_items, 1) * 16);

@@ -61,7 +61,7 @@ struct StaticFor {
 };
 
 constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
-constexpr int kGroupM = 4;  // M tiles walked together (n fastest inside the group)
+constexpr int kGroupM = 4;  // M tiles per patch of the K-grouped PATCH order
 
 // EPI_F32 overwrites the fp32 weight gradient, EPI_F32_ACC adds to it (two
 // kinds, so the overwrite form carries no loads of the old values)
@@ -129,8 +129,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 // valid: rows of the tile inside the expert (M-grouped) or the expert's row
 // count, i.e. the reduction length (K-grouped).
 //
-// M tile groups (kGroupM M tiles x all N tiles) in the order the XCDs take
-// them.  The tile table lists the M tiles longest expert first, so groups
+// M tile groups (2^gms M tiles x all N tiles) in the order the XCDs take
+// them; the tile table picks gms.  Groups of four M tiles share each weight
+// panel in L2 while some expert has several tiles; when none has more than
+// one, groups of one put all N tiles of an expert on one XCD at once, and
+// its activation rows are fetched into that L2 once (measured at 384
+// experts: ffn_up 28.3 -> 25.1 GB fetched, bwd_dxd 25.6 -> 24.3 GB; groups
+// of one with hot experts of many tiles: +0.7 ms per step at maxvio 20).  The tile table lists the M tiles longest expert first, so groups
 // come in falling cost: under skew the first are the heavy experts' full
 // tiles (MFMA-bound), the last the light experts' short ones (bound by the
 // weight stream).  XCD a walks a contiguous range of positions pg = a Q + b
@@ -148,20 +153,21 @@ __device__ __forceinline__ int group_dealt(int pg, int G) {
   return 8 * i + ((i & 1) ? 7 - a : a);
 }
 
-// M-grouped tile t of T = ntiles * ntn: groups of kGroupM M tiles (fewer in
+// M-grouped tile t of T = ntiles * ntn: groups of 2^gms M tiles (fewer in
 // the last group) walked with the M tile fastest, full groups dealt to the
 // XCDs by group_dealt.
-__device__ __forceinline__ void mtile_of(int t, int ntiles, int ntn, int& mt, int& nt) {
-  const int per_group = kGroupM * ntn, g4 = ntiles / kGroupM * per_group;
+__device__ __forceinline__ void mtile_of(int t, int ntiles, int ntn, int gms, int& mt, int& nt) {
+  const int gm = 1 << gms, per_group = ntn << gms, nfull = ntiles >> gms;
+  const int g4 = nfull * per_group;
   if (t < g4) {
     const int pg = t / per_group, r = t - pg * per_group;
-    const int g = group_dealt(pg, ntiles / kGroupM);
-    mt = g * kGroupM + r % kGroupM;
-    nt = r / kGroupM;
+    const int g = group_dealt(pg, nfull);
+    mt = (g << gms) + (r & (gm - 1));
+    nt = r >> gms;
   } else {
-    const int r = t - g4, gm = ntiles % kGroupM;
-    mt = ntiles / kGroupM * kGroupM + r % gm;
-    nt = r / gm;
+    const int r = t - g4, gl = ntiles & (gm - 1);
+    mt = (nfull << gms) + r % gl;
+    nt = r / gl;
   }
 }
 
@@ -208,7 +214,7 @@ __device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2,
     item = j;
   }
   int mt, nt;
-  mtile_of(t, *p.ntiles, p.ntn, mt, nt);
+  mtile_of(t, p.ntiles[0], p.ntn, p.ntiles[1], mt, nt);
   n0 = nt * BN;
   const int2 tt = p.tiles[mt];
   e = tt.x;
@@ -276,13 +282,13 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
     // The grid is sized for the most M tiles the routing could produce; only
     // the first nvalid block ids carry tiles, and only they are renumbered
     // (so every XCD gets its share of the real work).
-    const int per_group = kGroupM * p.ntn;
-    const int nvalid = (*p.ntiles + kGroupM - 1) / kGroupM * per_group;
+    const int gms = p.ntiles[1], gm = 1 << gms, per_group = p.ntn << gms;
+    const int nvalid = ((*p.ntiles + gm - 1) >> gms) * per_group;
     if (bid >= nvalid) return false;
     bid = xcd_remap(bid, nvalid);
     const int pg = bid / per_group, r = bid - pg * per_group;
-    const int mt = group_dealt(pg, nvalid / per_group) * kGroupM + r % kGroupM;
-    n0 = (r / kGroupM) * BN;
+    const int mt = (group_dealt(pg, nvalid / per_group) << gms) + (r & (gm - 1));
+    n0 = (r >> gms) * BN;
     if (mt >= *p.ntiles) return false;
     const int2 t = p.tiles[mt];
     e = t.x;
@@ -1190,7 +1196,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
   const int tt = blockIdx.x / MI, i = blockIdx.x % MI;
   if (sp.s < 2 || tt >= sp.rem) return;
   int mt, nt;
-  mtile_of(sp.full + tt, *p.ntiles, p.ntn, mt, nt);
+  mtile_of(sp.full + tt, p.ntiles[0], p.ntn, p.ntiles[1], mt, nt);
   const int2 tl = p.tiles[mt];
   const int64_t row0 = (int64_t)p.cu[tl.x] + tl.y;
   const int valid = min(BM, p.cu[tl.x + 1] - (int)row0);
@@ -1388,7 +1394,13 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     const int start = start_at[rank];
     for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
   }
-  if (e == 0) *ntiles = min(total, max_tiles);
+  // M tiles per group of the M-grouped products: 4, or 1 when no expert
+  // has more than one tile
+  const int multi = __syncthreads_or(e < E && nt > 1);
+  if (e == 0) {
+    ntiles[0] = min(total, max_tiles);
+    ntiles[1] = multi ? 2 : 0;
+  }
   if (eorder != nullptr) {
     // T: experts with more than twice the mean row count, rounded up so that
     // E - T is a multiple of 8 (the weight-gradient products split these
@@ -1420,8 +1432,9 @@ static void gemm_launch(const char* name, GemmArgs p, int max_mtiles, bool bf16,
     p.mtn = (p.M + bm - 1) / bm;
     blocks = p.E * p.mtn * p.ntn;
   } else {
-    const int groups = (max_mtiles + kGroupM - 1) / kGroupM;
-    blocks = groups * kGroupM * p.ntn;
+    // groups of four M tiles: enough blocks for either group size
+    const int groups = (max_mtiles + 3) >> 2;
+    blocks = (groups << 2) * p.ntn;
   }
   // a split last wave adds at most tail_cap blocks (its rem tiles become
   // s * rem parts, s * rem <= tail_cap)
