@@ -103,6 +103,10 @@ CASES = [
     # products split every tile along K (2 and 4 parts; H' = 2048 gives 32
     # and 64 K steps) and sum fp32 partial tiles in a second kernel
     ("c2_k_split_last_wave", "c2", dict(S=2100, H=256, Hf=2048, E=12)),
+    # the same with one M tile per expert (about 167 rows each): the
+    # M-grouped products walk groups of one M tile, and the split tail
+    # follows that order
+    ("c2_k_split_single_tiles", "c2", dict(S=1000, H=256, Hf=2048, E=12)),
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
