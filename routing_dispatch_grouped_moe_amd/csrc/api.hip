@@ -207,14 +207,14 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = reinterpret_cast<char*>(ws);
   const bool bf16 = d->dtype == MOE_BF16;
-  launch_fill_i32(counts, 0, d->E, s);
-  if (route_tiled(d->S, d->E, bf16)) {
+  if (route_tiled(d->S, d->E, bf16)) {  // its GEMM launch also zeroes the counts
     float* lg = logits ? logits : reinterpret_cast<float*>(w + L.route_logits);
     launch_route_tiled(x, Wg, bias, lg, topk_idx, gates, counts,
                        reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, L.epad, d->K,
                        (d->flags & MOE_F_RENORM) != 0, s);
     return launched();
   }
+  launch_fill_i32(counts, 0, d->E, s);
   int32_t* tickets = reinterpret_cast<int32_t*>(w + L.route_tickets);
   launch_transpose_wg(Wg, w + L.wgT, d->H, d->E, L.epad, bf16, bf16, tickets, L.route_groups,
                       s);

@@ -135,8 +135,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 // one, groups of one put all N tiles of an expert on one XCD at once, and
 // its activation rows are fetched into that L2 once (measured at 384
 // experts: ffn_up 28.3 -> 25.1 GB fetched, bwd_dxd 25.6 -> 24.3 GB; groups
-// of one with hot experts of many tiles: +0.7 ms per step at maxvio 20).  The tile table lists the M tiles longest expert first, so groups
-// come in falling cost: under skew the first are the heavy experts' full
+// of one with hot experts of many tiles: +0.7 ms per step at maxvio 20).
+// The tile table lists the M tiles longest expert first, so groups come in
+// falling cost: under skew the first are the heavy experts' full
 // tiles (MFMA-bound), the last the light experts' short ones (bound by the
 // weight stream).  XCD a walks a contiguous range of positions pg = a Q + b
 // (Q = G / 8 groups each).  Its i-th costliest share is group 8 i + a for

@@ -438,8 +438,9 @@ constexpr int kRgWaves = 8;
 __global__ __launch_bounds__(64 * kRgWaves) void route_gemm_kernel(const void* __restrict__ x,
                                                          const void* __restrict__ Wg,
                                                          const float* __restrict__ bias,
-                                                         float* __restrict__ out, int S, int H,
-                                                         int E, int ntn) {
+                                                         float* __restrict__ out,
+                                                         int32_t* __restrict__ counts, int S,
+                                                         int H, int E, int ntn) {
   constexpr int kTileA = kRgBM * kBK * 2, kTileB = kRgBN * kBK * 2, kStage = kTileA + kTileB;
   __shared__ __attribute__((aligned(1024))) char smem[kRgNS * kStage];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -447,6 +448,9 @@ __global__ __launch_bounds__(64 * kRgWaves) void route_gemm_kernel(const void* _
   const int t0 = mt * kRgBM, e0 = nt * kRgBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the top-K launch that follows adds each block's expert counts
+  if (blockIdx.x == 0)
+    for (int i = tid; i < E; i += 64 * kRgWaves) counts[i] = 0;
   constexpr int kWN = kRgWaves / 2, kWNT = kRgBN / kWN, NJ = kWNT / 32;
   const int wm = w / kWN, wn = w % kWN;
   const int rows = min(kRgBM, S - t0);
@@ -577,7 +581,7 @@ void launch_route_tiled(const void* x, const void* Wg, const float* bias, float*
   {
     TimedLaunch tl("route", s);
     hipLaunchKernelGGL(route_gemm_kernel, dim3(blocks), dim3(64 * kRgWaves), 0, s, x, Wg, bias, logits,
-                       (int)S, H, E, ntn);
+                       counts, (int)S, H, E, ntn);
   }
   const size_t lds = (size_t)kTopkTB * epad * sizeof(float);
   const int tb = (int)((S + kTopkTB - 1) / kTopkTB);
