@@ -33,6 +33,8 @@ __device__ __forceinline__ uint32_t kc_off(int row, int c) {
 // shifted against each other.
 template <int COLS>
 __device__ __forceinline__ uint32_t km_off(int k, int c) {
+  // the swizzle moves a chunk by up to 14 places: rows of at least 16 chunks
+  static_assert(COLS >= 128, "K-major tiles need at least 128 columns");
   return (uint32_t)k * (COLS * 2) + ((uint32_t)(c ^ (4 * (k & 3)) ^ (2 * ((k >> 3) & 1))) << 4);
 }
 
