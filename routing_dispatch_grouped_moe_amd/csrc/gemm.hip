@@ -61,7 +61,6 @@ struct StaticFor {
 };
 
 constexpr int kThreads = 512;  // eight wavefronts: 2 along M x 4 along N
-constexpr int kGroupM = 4;  // M tiles per patch of the K-grouped PATCH order
 
 // EPI_F32 overwrites the fp32 weight gradient, EPI_F32_ACC adds to it (two
 // kinds, so the overwrite form carries no loads of the old values)
@@ -232,11 +231,13 @@ __device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2,
 // expert.  Measured at 384 experts: whole dealing speeds dW2 up by 7-10% and
 // slows dW1/dW3 by 6-12%, so only dW2 asks for it.
 // Inside an expert's range the tiles run N fastest, or with PATCH in groups
-// of kGroupM M tiles x all N tiles (M fastest), so the tiles an XCD holds at
-// once form a compact patch whose operand rows its L2 shares.  Measured:
-// PATCH speeds up the few-row dW1/dW3 product (-9% at 384 experts) and slows
-// the others (dW2 there, the many-row products), whose N-fastest order keeps
-// each block's fp32 output rows contiguous.
+// of 1024 / BM M tiles (1024 rows of the M side) x all N tiles (M fastest),
+// so the tiles an XCD holds at once form a compact patch whose operand rows
+// its L2 shares.  Measured: PATCH speeds up the few-row dW1/dW3 product (-9%
+// at 384 experts) and slows the others (dW2 there, the many-row products),
+// whose N-fastest order keeps each block's fp32 output rows contiguous; with
+// 128-row tiles, patches of 8 M tiles beat 4, 6 and 12 (dW1/dW3 9.2 against
+// 9.7-10.1, 9.5 and 9.3 ms at 384 experts).
 template <bool KGROUP, int BM, int BN, bool PATCH = false>
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int64_t& row0,
                                         int& valid, int& m0, int& n0) {
@@ -267,10 +268,11 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
     }
     e = p.eorder ? p.eorder[slot] : slot;
     if constexpr (PATCH) {
-      const int per_group = kGroupM * p.ntn;
+      constexpr int kPatchM = 1024 / BM;
+      const int per_group = kPatchM * p.ntn;
       const int g = rp / per_group, r = rp - g * per_group;
-      const int gm = min(kGroupM, p.mtn - g * kGroupM);  // the last group may be short
-      m0 = (g * kGroupM + r % gm) * BM;
+      const int gm = min(kPatchM, p.mtn - g * kPatchM);  // the last group may be short
+      m0 = (g * kPatchM + r % gm) * BM;
       n0 = (r / gm) * BN;
     } else {
       m0 = (rp / p.ntn) * BM;
