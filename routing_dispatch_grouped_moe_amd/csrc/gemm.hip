@@ -130,11 +130,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int e, int64_t row, 
 //
 // M tile groups (2^gms M tiles x all N tiles) in the order the XCDs take
 // them; the tile table picks gms.  Groups of four M tiles share each weight
-// panel in L2 while some expert has several tiles; when none has more than
+// panel in L2 while experts have several tiles; when none has more than
 // one, groups of one put all N tiles of an expert on one XCD at once, and
 // its activation rows are fetched into that L2 once (measured at 384
 // experts: ffn_up 28.3 -> 25.1 GB fetched, bwd_dxd 25.6 -> 24.3 GB; groups
 // of one with hot experts of many tiles: +0.7 ms per step at maxvio 20).
+// When most experts have one tile and a few hot ones many (skewed routing),
+// groups of two do best: -0.3 to -0.9 ms per step at maxvio 20 and -1.2% on
+// 64 Zipf-skewed experts, where balanced multi-tile routing (8 experts of
+// 2048 rows, 16 of 512) runs 1-2% slower with them than with four.
 // The tile table lists the M tiles longest expert first, so groups come in
 // falling cost: under skew the first are the heavy experts' full
 // tiles (MFMA-bound), the last the light experts' short ones (bound by the
@@ -1397,12 +1401,14 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
     const int start = start_at[rank];
     for (int t = 0; t < nt && start + t < max_tiles; ++t) tiles[start + t] = make_int2(e, t * bm);
   }
-  // M tiles per group of the M-grouped products: 4, or 1 when no expert
-  // has more than one tile
-  const int multi = __syncthreads_or(e < E && nt > 1);
+  // M tiles per group of the M-grouped products: 1 when no expert has more
+  // than one tile; 2 when most experts with rows have one (a few hot ones
+  // hold the rest); else 4
+  const int multi = __syncthreads_count(e < E && nt > 1);
+  const int single = __syncthreads_count(e < E && nt == 1);
   if (e == 0) {
     ntiles[0] = min(total, max_tiles);
-    ntiles[1] = multi ? 2 : 0;
+    ntiles[1] = multi == 0 ? 0 : (single > multi ? 1 : 2);
   }
   if (eorder != nullptr) {
     // T: experts with more than twice the mean row count, rounded up so that

@@ -36,7 +36,7 @@ struct WsLayout {
   size_t base;        // dispatch: [nb, E] int32 first row of each (block, expert)
   size_t tiles;       // grouped GEMM: [max_tiles] int2 (expert, first row) per M tile
   size_t ntiles;      // int32 number of valid M tiles, then int32 log2 of the M tiles per
-                      // tile group of the M-grouped products (0 or 2)
+                      // tile group of the M-grouped products (0, 1 or 2)
   size_t eorder;      // [E + 1] int32 experts by descending row count (ties: lower index
                       // first), then the count of them the weight gradients split by XCD
   size_t dl_row;      // [R] fp32 dlogit of each dispatched row

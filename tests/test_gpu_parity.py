@@ -107,6 +107,9 @@ CASES = [
     # M-grouped products walk groups of one M tile, and the split tail
     # follows that order
     ("c2_k_split_single_tiles", "c2", dict(S=1000, H=256, Hf=2048, E=12)),
+    # and with most experts at one M tile but two at four (groups of two M
+    # tiles, 13 tiles in all)
+    ("c4_k_split_pairs", "c4", dict(S=1000, H=256, Hf=2048, E=12, K=2, beta=1.0)),
     ("c3_zipf_small", "c3", dict(S=257, H=256, Hf=256)),
     ("c4_moonep_small", "c4", dict(S=200, H=512, Hf=256, beta=1.0)),
     ("c4_moonep_skewed_small", "c4", dict(S=640, H=256, Hf=384, beta=4.0)),
