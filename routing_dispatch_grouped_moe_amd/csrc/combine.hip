@@ -66,7 +66,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
   return make_rsrc(reinterpret_cast<const char*>(base) + (int64_t)r * H * Piece<BF16>::kEb, bytes);
 }
 
-constexpr int kCombU = 2;  // column chunks (of 64 pieces) per iteration
+// column chunks (of 64 pieces) per iteration; one chunk measured 10-12 us
+// faster than two for dx at 384 experts, top-8 (252 against 263 us), and the
+// same at 8 experts
+constexpr int kCombU = 1;
 // combine and dx: one wavefront per (token, chunk of kCombChunk pieces), so
 // a wide row spreads over several wavefronts and the last wave of a launch
 // is short
