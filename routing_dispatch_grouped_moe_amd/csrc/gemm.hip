@@ -242,12 +242,24 @@ __device__ __forceinline__ bool mtile_split(const GemmArgs& p, int bid, int nk2,
 // whose N-fastest order keeps each block's fp32 output rows contiguous; with
 // 128-row tiles, patches of 8 M tiles beat 4, 6 and 12 (dW1/dW3 9.2 against
 // 9.7-10.1, 9.5 and 9.3 ms at 384 experts).
-template <bool KGROUP, int BM, int BN, bool PATCH = false>
+template <bool KGROUP, int BM, int BN, bool PATCH = false, bool PATCH_SKEW = false>
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int64_t& row0,
                                         int& valid, int& m0, int& n0) {
   if constexpr (KGROUP) {
     const int per_e = p.mtn * p.ntn;
     int slot, rp;
+    // PATCH_SKEW: patches only under skewed routing, i.e. when the hottest
+    // expert has more than twice the mean rows (measured with the one-
+    // wavefront-per-SIMD dW1/dW3: -9% on 64 Zipf-skewed experts, +6% on 16
+    // balanced ones, the same on 8 balanced ones)
+    bool patch = PATCH;
+    if constexpr (PATCH_SKEW) {
+      if (p.eorder != nullptr) {
+        const int eh = p.eorder[0];
+        const int64_t rows = (int64_t)p.cu[p.E] - p.cu[0];
+        patch = (int64_t)(p.cu[eh + 1] - p.cu[eh]) * p.E > 2 * rows;
+      }
+    }
     if (p.deal_whole && p.eorder != nullptr && (per_e & 7) == 0) {
       // Block bid runs on XCD bid % 8 as that XCD's block bid / 8.  The first
       // T experts of the dealing order (the heavy ones) are split eight ways,
@@ -268,10 +280,10 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, int bid, int& e, int6
     } else {
       slot = bid / per_e;
       const int rem = bid - slot * per_e;
-      rp = PATCH ? xcd_remap(rem, per_e) : rem;
+      rp = patch ? xcd_remap(rem, per_e) : rem;
     }
     e = p.eorder ? p.eorder[slot] : slot;
-    if constexpr (PATCH) {
+    if (patch) {
       constexpr int kPatchM = 1024 / BM;
       const int per_group = kPatchM * p.ntn;
       const int g = rp / per_group, r = rp - g * per_group;
@@ -653,7 +665,8 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   int e, valid, m0 = 0, n0, part = -1, item = 0, nparts = 1;
   int64_t row0;
   if constexpr (KGROUP) {
-    if (!tile_of<KGROUP, BM, BN>(p, blockIdx.x, e, row0, valid, m0, n0)) return;
+    if (!tile_of<KGROUP, BM, BN, false, KGROUP && DUAL>(p, blockIdx.x, e, row0, valid, m0, n0))
+      return;
   } else {
     const int nks = p.K / kBK, nkt = TWOSEG ? 2 * nks : nks;
     if (!mtile_split<BM, BN, kSplit>(p, blockIdx.x, (nkt + 1) & ~1, e, row0, valid, n0, part, item,

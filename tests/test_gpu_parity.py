@@ -133,6 +133,10 @@ CASES = [
     # top-16; 2080 rows): spread over ~850 experts of at most ten rows each,
     # and Zipf-concentrated on ~28 experts with every token in the hottest
     # ones (several 64-row tiles each) and ~1000 experts empty
+    # Zipf-skewed with at least 512 rows per expert: the one-wavefront-per-
+    # SIMD weight gradients, dW1/dW3 in patches (the hottest expert holds
+    # half the rows)
+    ("c3_many_rows_skewed", "c3", dict(S=2100, H=256, Hf=384, E=8, K=2)),
     ("max_experts_top16_spread", "c4", dict(S=130, H=128, Hf=128, E=1024, K=16, beta=0.0)),
     ("max_experts_top16_zipf", "c3", dict(S=130, H=128, Hf=128, E=1024, K=16)),
 ]
