@@ -93,9 +93,15 @@ WsLayout ws_layout(int64_t S, int H, int Hf, int E, int K, int dtype, uint32_t f
   L.tail_items = (int)std::min<int64_t>(256, (int64_t)8 * L.max_tiles * ((H + 255) / 256));
   L.gemm_part = off; off = align256(off + (size_t)std::max(L.tail_items, 1) * 256 * 256 * 4);
   L.route_groups = (int)((S + 31) / 32);
-  L.route_parts = dtype == MOE_BF16 ? route_parts(S, H, L.epad) : 1;
+  const bool tiled = route_tiled(S, E, dtype == MOE_BF16);
+  L.route_parts = dtype == MOE_BF16 && !tiled ? route_parts(S, H, L.epad) : 1;
   L.route_part = off;
-  off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
+  if (tiled) {
+    const int P = route_tiled_parts(S, H, E);
+    off = align256(off + (P > 1 ? (size_t)P * S * E * 4 : 4));
+  } else {
+    off = align256(off + (L.route_parts > 1 ? (size_t)L.route_groups * L.route_parts * 32 * L.epad * 4 : 4));
+  }
   L.route_tickets = off; off = align256(off + (size_t)std::max(L.route_groups, 1) * 4);
   L.route_logits = off;
   if (route_tiled(S, E, dtype == MOE_BF16)) off = align256(off + (size_t)S * E * 4);
@@ -211,7 +217,8 @@ moe_status_t moe_route(const moe_dims_t* d, const void* x, const void* Wg, const
     float* lg = logits ? logits : reinterpret_cast<float*>(w + L.route_logits);
     launch_route_tiled(x, Wg, bias, lg, topk_idx, gates, counts,
                        reinterpret_cast<uint32_t*>(w + L.status), d->S, d->H, d->E, L.epad, d->K,
-                       (d->flags & MOE_F_RENORM) != 0, s);
+                       (d->flags & MOE_F_RENORM) != 0, reinterpret_cast<float*>(w + L.route_part),
+                       s);
     return launched();
   }
   launch_fill_i32(counts, 0, d->E, s);

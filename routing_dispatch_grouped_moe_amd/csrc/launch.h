@@ -44,7 +44,8 @@ struct WsLayout {
   size_t dwg_estart;  // [E+1] int32 first item of each expert (exclusive scan)
   size_t dwg_part;    // [dwg_max_items, H] fp32 partial router-weight gradient per item
   size_t gemm_part;   // [tail_items, 256 * 256] fp32 K-split partial tiles of the last GEMM wave
-  size_t route_part;  // [groups, route_parts, 32, epad] fp32 partial logits of a split router
+  size_t route_part;  // fp32 partial logits of a split router: [groups, route_parts, 32, epad]
+                      // (fused), or [route_tiled_parts, S, E] (tiled)
   size_t route_tickets; // [groups] int32 parts finished per 32-token group
   size_t route_logits;  // [S, E] fp32 logits of the tiled router when the caller keeps none
   size_t dwg_dense_part; // [splits, H, epad] fp32 token-slice partials of the dense dWg (raw gates)
@@ -77,9 +78,12 @@ int route_parts(int64_t S, int H, int epad);
 // caller's, or the workspace's route_logits) plus a top-K launch; it reads Wg
 // in its [H][E] layout (no transposed copy)
 bool route_tiled(int64_t S, int E, bool bf16);
+int route_tiled_parts(int64_t S, int H, int E);
+// part: [route_tiled_parts, S, E] fp32 partial logits (used when there are
+// several parts; null: one part)
 void launch_route_tiled(const void* x, const void* Wg, const float* bias, float* logits,
                         int32_t* idx, float* gates, int32_t* counts, uint32_t* status, int64_t S,
-                        int H, int E, int epad, int K, bool renorm, hipStream_t s);
+                        int H, int E, int epad, int K, bool renorm, float* part, hipStream_t s);
 void launch_route(const void* x, const void* wgT, const float* bias, float* logits, int32_t* idx,
                   float* gates, int32_t* counts, uint32_t* status, int64_t S, int H, int E, int epad,
                   int K, bool renorm, bool bf16, int nparts, float* rpart, int32_t* tickets,

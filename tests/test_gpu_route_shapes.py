@@ -8,9 +8,11 @@ against the oracle's selection on the GPU's own fp32 logits (the integer
 decision taken in the same precision), gates to 1e-5 and per-expert counts
 bit for bit.  S = 100 leaves a ragged last block of 4 tokens.  A second test
 runs token counts on both sides of the H-split rule (split up to 1024 tokens);
-a third runs the tiled router (many experts and tokens: a tiled GEMM into fp32
-logits, then the top-K launch); a fourth checks the load statistics of
-routing histograms (maxvio, load entropy).
+a third runs the tiled router (bf16, at least 256 experts, a multiple of 8: a
+tiled GEMM into fp32 logits, H cut into parts when the tiles are few, then the
+top-K launch); a fourth checks the load statistics of routing histograms
+(maxvio, load entropy).  From 256 experts up the first two tests take expert
+counts that are not multiples of 8, which stay on the fused router.
 """
 import sys
 
@@ -29,9 +31,10 @@ if not torch.cuda.is_available():
 
 from routing_dispatch_grouped_moe_amd import _lib as L  # noqa: E402
 
-# (E, K): one expert count per router tiling
-SHAPES = [(8, 2), (24, 4), (40, 6), (64, 8), (100, 8), (160, 8), (224, 8), (384, 8), (448, 16),
-          (640, 8), (1000, 16)]
+# (E, K): one expert count per fused-router tiling (E padded to 16: 380 -> 384,
+# 444 -> 448, 636 -> 640, 1002 -> 1008)
+SHAPES = [(8, 2), (24, 4), (40, 6), (64, 8), (100, 8), (160, 8), (224, 8), (380, 8), (444, 16),
+          (636, 8), (1002, 16)]
 
 
 @pytest.mark.parametrize("E,K", SHAPES, ids=[f"E{e}_K{k}" for e, k in SHAPES])
@@ -65,7 +68,7 @@ def test_route_shapes(E, K):
 # (S, H, E, K): token counts around the router's H-split rule (up to 1024
 # tokens, i.e. 32 token groups, split the H reduction over 2 to 16 blocks per
 # group; more tokens do not split), at hidden sizes that allow every part count
-SPLITS = [(64, 4096, 384, 8), (500, 2048, 384, 8), (1000, 2048, 64, 4), (1024, 1024, 160, 8),
+SPLITS = [(64, 4096, 380, 8), (500, 2048, 380, 8), (1000, 2048, 64, 4), (1024, 1024, 160, 8),
           (1056, 1024, 160, 8)]
 
 
@@ -97,11 +100,15 @@ def test_route_split_boundary(S, H, E, K):
     np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
 
 
-# (S, H, E, K): the tiled router (at least 2048 tokens, at least 256 experts,
-# E a multiple of 8): one or several 128-expert tiles, a partial last tile,
-# ragged token tiles, and (32768 tokens) three blocks per compute unit
+# (S, H, E, K): the tiled router (at least 256 experts, E a multiple of 8): one
+# or several 128-expert tiles, a partial last tile, ragged token tiles, and
+# (32768 tokens) three blocks per compute unit; with few tokens the H extent
+# is cut into parts: 16 parts of 4 K steps (64 x 4096 x 384), 16 parts of 7
+# (decode, 128 x 7168 x 384), 4 parts (300 x 1024 x 1000) and 4 unequal parts
+# of 4, 5, 4 and 5 K steps (100 x 1152 x 256)
 TILED = [(2048, 256, 256, 8), (2100, 512, 384, 8), (4000, 128, 1000, 16), (8192, 256, 384, 8),
-         (2049, 1024, 640, 4), (32768, 128, 384, 8)]
+         (2049, 1024, 640, 4), (32768, 128, 384, 8), (64, 4096, 384, 8), (128, 7168, 384, 8),
+         (300, 1024, 1000, 8), (100, 1152, 256, 4)]
 
 
 @pytest.mark.parametrize("S,H,E,K", TILED, ids=[f"S{s}_H{h}_E{e}_K{k}" for s, h, e, k in TILED])
