@@ -786,6 +786,16 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   constexpr int kB0 = (kDmaB + 2) / 3, kB1 = (kDmaB + 1) / 3, kB2 = kDmaB - kB0 - kB1;
   static_assert(kFrag <= kMfma && kDmaA <= kMfma && kB0 <= kMfma, "slice interleave");
 
+  // The SwiGLU backward epilogue's first 128 rows of h1 and h3 (256 columns,
+  // 512-byte rows) as four 64-row halves of 32 KB: instruction i of this
+  // wavefront fills 1-KB slot 8 w + i of a half, staged rows 2 j and 2 j + 1
+  // with 16-byte chunk c of row q at c ^ (q & 15) (the staged-tile layout).
+  const int hl = lane >> 5, slot = lane & 31;
+  auto epi_issue = [&](int i, const u32x4& rs, char* ds) {
+    const int j = w * 8 + i, q = 2 * j + hl;
+    const uint32_t voff = ((uint32_t)q * (uint32_t)p.ldc + 8u * (uint32_t)(slot ^ (q & 15))) * 2u;
+    dma16(rs, voff, ds + j * 1024);
+  };
   // One K16 slice in a pinned issue order: MFMA t on the current fragments,
   // then fragment t of the next slice (from A tile ra_t and B buffer rb_t),
   // then, spread evenly over the slice's MFMAs, its n direct loads:
@@ -817,6 +827,8 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
           if constexpr (OP == 0) {
             const u32x4 r1[1] = {rs[0]};
             da.issue_one(d0 + n, r1, ds, w);
+          } else if constexpr (OP == 2) {
+            epi_issue(d0 + n, rs[0], ds);
           } else {
             u32x4 rn[NB];
 #pragma unroll
@@ -867,6 +879,31 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaB) : "memory");
     slice(af1, bf1, nxt, bn, 0, af0, bf0, ra2, cur, 0, act, IA{}, NA{});
   };
+  // The last two steps of a tile would load operand tiles for steps past
+  // the end, never read; in the SwiGLU backward product they load the
+  // epilogue's first h1 rows (into the B buffer each step frees, in the
+  // B loads' slots) and h3 rows (into its A stage), the same count of
+  // 1-KB loads at the same points, so the waits and the buffer protocol
+  // are those of any other step.  The epilogue's first phase then finds its
+  // inputs in LDS instead of waiting for them after the K loop (measured:
+  // dA 1885 -> 1836 us at 8 experts x 2048 rows, H 4096, H' 14336; within
+  // noise at 384 experts, where the product is bound by HBM).
+  constexpr bool kEpiFetch = EPI == EPI_SWIGLU_BWD;
+  static_assert(!kEpiFetch || (kDmaA == 8 && kDmaB == 8 && BN == 256), "h1/h3 halves in the load slots");
+  using IE = std::integral_constant<int, 2>;
+  auto step_epi = [&](int i3, auto cur_tag, auto act, const u32x4 (&rz)[1], const u32x4 (&ru)[1]) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    char* cur = CUR ? stage1 : stage0;
+    char* nxt = CUR ? stage0 : stage1;
+    char* bc = bsel(i3);
+    char* bn = bsel(i3 == 2 ? 0 : i3 + 1);
+    char* bnn = bsel(i3 == 0 ? 2 : i3 - 1);
+    slice(af0, bf0, cur, bc, 1, af1, bf1, rz, bnn, 0, act, IE{}, N0{});
+    slice(af1, bf1, cur, bc, 2, af0, bf0, rz, bnn, kB0, act, IE{}, N1{});
+    slice(af0, bf0, cur, bc, 3, af1, bf1, rz, bnn, kB0 + kB1, act, IE{}, N2{});
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaB) : "memory");
+    slice(af1, bf1, nxt, bn, 0, af0, bf0, ru, cur, 0, act, IE{}, NA{});
+  };
 
   // K steps [k_lo, k_end) of this block: all of them, or one part of a split
   // tile (even boundaries, so the two-stage unroll holds)
@@ -899,13 +936,37 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
   // one copy of the K loop per active row-block count, without branches
   // between its MFMAs (a wavefront takes the copy of its own count; every
   // copy runs the same loads and barriers)
+  // descriptors of the epilogue's h1 (rz) and h3 (ru) rows 0-63 and 64-127
+  // (rows past the tile's valid ones and columns past N read zeros), and the
+  // B buffers that the two h1 halves land in
+  u32x4 rz[2][1], ru[2][1];
+  char* ez[2] = {stage2, stage2};
+  if constexpr (kEpiFetch) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t rows_left = (int64_t)valid - 64 * h;
+      const int64_t lim = rows_left > 0 ? ((rows_left - 1) * p.ldc + (p.N - n0)) * 2 : 0;
+      const int64_t off = ((row0 + 64 * h) * p.ldc + n0) * 2;
+      rz[h][0] = rsrc_words(reinterpret_cast<const char*>(p.X0) + off, (uint32_t)lim);
+      ru[h][0] = rsrc_words(reinterpret_cast<const char*>(p.X1) + off, (uint32_t)lim);
+    }
+    const int i3a = (k_end - 2 - k_lo) % 3, i3b = i3a == 2 ? 0 : i3a + 1;
+    ez[0] = bsel(i3a == 0 ? 2 : i3a - 1);
+    ez[1] = bsel(i3b == 0 ? 2 : i3b - 1);
+  }
   auto kloop = [&](auto act) {
     int i3 = 0;
-    for (int kt = k_lo; kt < k_end; kt += 2) {
+    const int k_main = kEpiFetch ? k_end - 2 : k_end;
+    for (int kt = k_lo; kt < k_main; kt += 2) {
       step(kt, i3, I0{}, act);
       i3 = i3 == 2 ? 0 : i3 + 1;
       step(kt + 1, i3, I1{}, act);
       i3 = i3 == 2 ? 0 : i3 + 1;
+    }
+    if constexpr (kEpiFetch) {
+      step_epi(i3, I0{}, act, rz[0], ru[0]);
+      i3 = i3 == 2 ? 0 : i3 + 1;
+      step_epi(i3, I1{}, act, rz[1], ru[1]);
     }
   };
   if (KGROUP || mi_act == MI) {
@@ -1116,16 +1177,18 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
     } else {
       // SwiGLU backward: two phases of 128 tile rows, phase ph the tile rows
       // 128 ph .. 128 ph + 127 (row blocks 2 ph and 2 ph + 1 of both
-      // wavefront rows, interleaved).  A phase's h1 rows come into stage 0
-      // and its h3 rows into stage 1 by direct loads (no staging registers),
-      // dh1 and dh3 overwrite them in place and leave as whole rows.  A tile
-      // of at most 128 valid rows has no second phase.
+      // wavefront rows, interleaved).  The first phase's h1 and h3 rows
+      // arrived during the K loop's last two steps, in 64-row halves (h1 in
+      // the B buffers ez[], h3 in the A parts of stages 0 and 1); the second
+      // phase's come into stage 0 (h1) and stage 1 (h3) by direct loads (no
+      // staging registers).  dh1 and dh3 overwrite them in place and leave
+      // as whole rows.  A tile of at most 128 valid rows has no second phase.
       static_assert(EPI == EPI_SWIGLU_BWD && NB == 1 && BM == 256 && BN == 256, "dA epilogue tile");
       static_assert(MI == 4 && RS == 512, "two 128-row phases of 256 columns");
-      // staged row q of phase ph is tile row 128 ph + q; wavefront w loads
+      // staged row q of phase 1 is tile row 128 + q; wavefront w loads
       // 32 KB of one matrix: instruction u covers staged rows
       // 2 (32 (w & 1) + u) and the next one
-      const int mat = w >> 1, hl = lane >> 5, slot = lane & 31;
+      const int mat = w >> 1;
       const char* xbase = reinterpret_cast<const char*>(mat ? p.X1 : p.X0) +
                           ((int64_t)row0 * p.ldc + n0) * 2;
       char* dstage = mat ? stage1 : stage0;
@@ -1141,7 +1204,7 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
           dma16(rs, voff, dstage + j * 1024);
         }
       };
-      dma_phase(0);
+      using R64 = std::integral_constant<int, 64>;
       StaticFor<0, 2>::run([&](auto ph_tag) {
         constexpr int ph = decltype(ph_tag)::value;
         if (ph == 1 && valid <= 128) return;  // uniform over the block
@@ -1152,12 +1215,15 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
           constexpr int x = decltype(x_tag)::value, ib = x / (NJ * 4), j = (x / 4) % NJ, g = x % 4;
           constexpr int i = 2 * ph + ib;
           if (i < mi_act) {
-            // tile row block 2 i + wm = 4 ph + 2 ib + wm
-            const int q = (2 * ib + wm) * 32 + (lane & 31);
+            // tile row block 2 i + wm = 4 ph + 2 ib + wm; in the first phase
+            // half ib, row wm * 32 + lane % 32 of it
+            const int q = ph == 0 ? wm * 32 + (lane & 31) : (2 * ib + wm) * 32 + (lane & 31);
+            char* const sz = ph == 0 ? ez[ib] : stage0;
+            char* const su = ph == 0 ? (ib ? stage1 : stage0) : stage1;
             const int c = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
             float z[4], u[4], d1[4], d3[4];
-            get4(stage0, q, c, z);
-            get4(stage1, q, c, u);
+            get4(sz, q, c, z);
+            get4(su, q, c, u);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const float v = acc[0][i][j][4 * g + t];
@@ -1166,13 +1232,20 @@ void gemm_bf16_w4_kernel(GemmArgs p) {
               d3[t] = vs * z[t];
               d1[t] = vs * u[t] * (1.0f + z[t] - z[t] * sg);
             }
-            put4(stage0, q, c, d1);
-            put4(stage1, q, c, d3);
+            put4(sz, q, c, d1);
+            put4(su, q, c, d3);
           }
         });
         __syncthreads();
-        store_rows(stage0, R128{}, p.C0, 128 * ph, R128{}, R0{});
-        store_rows(stage1, R128{}, p.C1, 128 * ph, R128{}, R0{});
+        if constexpr (ph == 0) {
+          store_rows(ez[0], R64{}, p.C0, 0, R64{}, R0{});
+          store_rows(ez[1], R64{}, p.C0, 64, R64{}, R0{});
+          store_rows(stage0, R64{}, p.C1, 0, R64{}, R0{});
+          store_rows(stage1, R64{}, p.C1, 64, R64{}, R0{});
+        } else {
+          store_rows(stage0, R128{}, p.C0, 128, R128{}, R0{});
+          store_rows(stage1, R128{}, p.C1, 128, R128{}, R0{});
+        }
         if constexpr (ph == 0) {
           if (valid > 128) {
             // every wavefront has read the stages for its stores
