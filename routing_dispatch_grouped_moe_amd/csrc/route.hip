@@ -623,11 +623,12 @@ void launch_route_tiled(const void* x, const void* Wg, const float* bias, float*
     TimedLaunch tl("route", s);
     hipLaunchKernelGGL(route_gemm_kernel, dim3(blocks, P), dim3(64 * kRgWaves), 0, s, x, Wg, bias,
                        P > 1 ? part : logits, counts, (int)S, H, E, ntn);
-    if (P > 1) {
-      const int64_t n4 = S * (int64_t)E / 4;
-      hipLaunchKernelGGL(route_part_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                         part, P, bias, logits, (int)S, E);
-    }
+  }
+  if (P > 1) {
+    TimedLaunch tl("route_part_sum", s);
+    const int64_t n4 = S * (int64_t)E / 4;
+    hipLaunchKernelGGL(route_part_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       part, P, bias, logits, (int)S, E);
   }
   const size_t lds = (size_t)kTopkTB * epad * sizeof(float);
   const int tb = (int)((S + kTopkTB - 1) / kTopkTB);
