@@ -114,11 +114,16 @@ const char* moe_status_string(moe_status_t st);
 moe_status_t moe_read_status(const void* ws, uint32_t* status, void* stream);
 
 /*
- * moe_route - router projection, softmax and top-K gating in one kernel.
+ * moe_route - router projection, softmax and top-K gating.
  * [FW] "What's in the box", routing/gating item (softmax over the experts and
  * the top-k pick done in a single launch) and "Comparison with alternatives"
  * (wavefront-level primitives for top-k); [T4] "The router is the main
  * culprit" (fused softmax + top-k; keep the routing sparse).
+ * Fewer than 256 experts, fp32, or E not a multiple of 8: one fused launch.
+ * Otherwise a tiled GEMM writes fp32 logits (the H reduction cut into parts,
+ * summed in a fixed order, when the tokens are few) and one launch does the
+ * softmax, top-K, gates and counts.  Both give the same results to rounding
+ * of the fp32 logits.
  *
  *   x        [S, H]   activations (dtype)
  *   Wg       [H, E]   router weight (dtype)
