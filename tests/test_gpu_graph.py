@@ -31,7 +31,10 @@ OUTS = ["logits", "topk_idx", "gates", "counts", "cu", "row_of", "tok_of", "xd",
     ("c2", dict(S=300, H=256, Hf=384), L.MOE_F_RENORM),
     ("c4", dict(S=640, H=256, Hf=384, beta=4.0), L.MOE_F_RENORM | L.MOE_F_RECOMPUTE),
     ("c3", dict(S=257, H=256, Hf=256), 0),
-], ids=["c2_renorm", "c4_skewed_recompute", "c3_raw_gates"])
+    # 128 tokens x 384 experts: the tiled router cuts H = 2048 into 8 parts
+    # (partial logits, then the part sum, then the top-K launch)
+    ("c4", dict(S=128, H=2048, Hf=256), L.MOE_F_RENORM),
+], ids=["c2_renorm", "c4_skewed_recompute", "c3_raw_gates", "c4_router_parts"])
 def test_graph_replay_matches_eager(cfg, ov, flags):
     print(f"[graph] {cfg} {ov} flags={flags}", flush=True)
     sys.stdout.flush()
