@@ -343,8 +343,8 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
                    bf16, s);
     launch_bwd_dw13(nullptr, nullptr, nullptr, sv->cu_seqlens, nullptr, dW1, dW3, 0, d->H, d->Hf, d->E,
                     accum, bf16, s);
-    launch_dwg(nullptr, sv->cu_seqlens, nullptr, dWg, L, reinterpret_cast<char*>(ws), 0, d->H,
-               d->E, accum, bf16, s);
+    launch_dwg(nullptr, nullptr, 0, sv->cu_seqlens, nullptr, dWg, L, reinterpret_cast<char*>(ws), 0,
+               d->H, d->E, accum, bf16, s);
     return launched();
   }
   const bool recompute = (d->flags & MOE_F_RECOMPUTE) != 0;
@@ -396,7 +396,7 @@ moe_status_t moe_backward(const moe_dims_t* d, const moe_saved_t* sv, const void
   } else {
     launch_dx(b->dxd, sv->row_of, sv->topk_idx, b->dlogits, w + L.wgT, dx, d->S, H, E, K, R, bf16,
               s);
-    launch_dwg(sv->xd, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
+    launch_dwg(sv->x, sv->tok_of, d->S, sv->cu_seqlens, dl_row, dWg, L, w, R, H, E, accum, bf16, s);
   }
   return launched();
 }

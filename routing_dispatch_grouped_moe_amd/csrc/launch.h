@@ -142,7 +142,8 @@ void launch_dx_dense(const void* dxd, const int32_t* row_of, const float* dlogit
 int dwg_dense_splits(int64_t S, int H, int epad);
 void launch_dwg_dense(const void* x, const float* dlogits, float* dWg, const WsLayout& L,
                       char* ws, int64_t S, int H, int E, bool accum, bool bf16, hipStream_t s);
-void launch_dwg(const void* xd, const int32_t* cu, const float* dl_row, float* dWg,
+void launch_dwg(const void* x, const int32_t* tok_of, int64_t S, const int32_t* cu,
+                const float* dl_row, float* dWg,
                 const WsLayout& L, char* ws, int64_t R, int H, int E, bool accum, bool bf16,
                 hipStream_t s);
 
