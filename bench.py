@@ -67,7 +67,8 @@ def kernel_model(name, cfg, counts):
         # the K router-weight rows each token gathers come from the small
         # cached [E, H] table: counted once
         "dispatch_bwd_dx": (2 * R * H, R * H * b + S * H * b + E * H * b + 8 * S * K),
-        "router_dWg_partial": (2 * R * H, R * H * b + 4 * R),
+        # each row's values are read from x through tok_of: x counted once
+        "router_dWg_partial": (2 * R * H, S * H * b + 8 * R),
         # whole C-ABI calls: what the call as a whole must move (its
         # set-up kernels -- counts fill, router-weight transpose, dispatch
         # bitmaps and scan -- add no algorithmic bytes)
