@@ -155,6 +155,6 @@ void launch_mod_backward(int B, int T, int C, int H, bool bf16, bool accum, cons
                          const void* w_r, const float* r, const int32_t* keep, const void* m,
                          const void* dout, const void* dxk, void* dm, float* dr, void* dx,
                          float* dw_r, float* part, hipStream_t s);
-constexpr int kModSplitsHost = 64;  // row splits of the MoD score-weight gradient
+constexpr int kModSplitsHost = 128;  // row splits of the MoD score-weight gradient
 
 }  // namespace moe
