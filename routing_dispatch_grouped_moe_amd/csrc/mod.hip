@@ -7,10 +7,10 @@
 //
 // gfx950 design: scores and every row copy run one wavefront per token with
 // 16-byte pieces; the per-sequence selection runs in one 1024-thread block
-// per sequence: 64-bit order keys (score bits : ~position) in LDS, a
-// bitonic sort of them (descending), the first C positions marked in an LDS
-// bitmap, then a block scan of per-thread counts writes them out in
-// ascending position order.  The merge and the backward find a token's kept
+// per sequence: 64-bit order keys (score bits : ~position) in LDS, a radix
+// select of the C-th largest key (eight 8-bit digit passes), then a block
+// scan of per-thread counts of the keys at or above it writes the kept
+// positions out in ascending order.  The merge and the backward find a token's kept
 // slot by binary search in its sequence's ascending keep list.
 #include "dev_common.h"
 #include "launch.h"
@@ -39,51 +39,70 @@ __global__ __launch_bounds__(256) void mod_score_kernel(const void* __restrict__
 
 // One block (1024 threads) per sequence; T <= 8192.  The (score, position)
 // keys are unique (ties broken toward the earlier position), so the kept set
-// is the C largest keys: a bitonic sort of the keys in LDS (descending,
-// padded to a power of two with zero keys, which sort last), then the top C
-// positions are marked in a bitmap and written out in position order
-// through a block scan of per-thread counts.
+// is the keys at or above the C-th largest.  That key is found digit by digit
+// from the top: eight passes of 8 bits, each an LDS histogram of the keys
+// that still match the digits fixed so far, in which one wavefront finds the
+// bin holding the C-th key from the top.  Every thread then counts the kept
+// keys of its own run of positions, and a block scan writes them out in
+// position order.  Measured at 4 sequences x 2048 tokens: 13 us against 38
+// us for a bitonic sort of the keys (66 barrier rounds).
 __global__ __launch_bounds__(1024) void mod_select_kernel(const float* __restrict__ r,
                                                           int32_t* __restrict__ keep, int T,
                                                           int C) {
   __shared__ uint64_t keys[8192];
-  __shared__ uint32_t kept[8192 / 32];
+  __shared__ int hist[256];
   __shared__ int scan[1024];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int N = 1;
-  while (N < T) N <<= 1;
-  for (int t = tid; t < N; t += 1024) keys[t] = t < T ? topk_key(r[(int64_t)b * T + t], t) : 0ull;
-  for (int i = tid; i < 8192 / 32; i += 1024) kept[i] = 0u;
-  __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int x = tid; x < N; x += 1024) {
-        const int y = x ^ j;
-        if (y > x) {
-          const uint64_t kx = keys[x], ky = keys[y];
-          // blocks with (x & k) == 0 end descending, the others ascending,
-          // so the final merge leaves the whole array descending
-          if (((x & k) == 0) ? (kx < ky) : (kx > ky)) {
-            keys[x] = ky;
-            keys[y] = kx;
-          }
-        }
-      }
-      __syncthreads();
+  __shared__ int pick[2];  // the digit of the C-th key, and the keys above its bin
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  for (int t = tid; t < T; t += 1024) keys[t] = topk_key(r[(int64_t)b * T + t], t);
+  uint64_t prefix = 0, mask = 0;  // the digits fixed so far
+  int need = C;                   // rank of the wanted key among the matching ones
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();  // (the first time also publishes the keys)
+    for (int t = tid; t < T; t += 1024) {
+      const uint64_t k = keys[t];
+      if ((k & mask) == prefix) atomicAdd(&hist[(int)(k >> shift) & 255], 1);
     }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l .. 4l + 3; above = the matching keys in higher
+      // bins, from a scan of the lane sums in reverse lane order
+      int h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
+      const int sum4 = h[0] + h[1] + h[2] + h[3];
+      int v = __shfl(sum4, 63 - lane, 64);  // lane l: the sum of lane 63 - l
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+      }
+      // v at lane l: the sum of lanes 63 - l .. 63; lanes above L: lane 62 - L
+      const int up = __shfl(v, lane < 63 ? 62 - lane : 0, 64);
+      int above = lane < 63 ? up : 0;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < need && above + h[i] >= need) {
+          pick[0] = 4 * lane + i;
+          pick[1] = above;
+        }
+        above += h[i];
+      }
+    }
+    __syncthreads();
+    need -= pick[1];
+    prefix |= (uint64_t)pick[0] << shift;
+    mask |= 255ull << shift;
   }
-  for (int i = tid; i < C; i += 1024) {
-    const int t = key_expert(keys[i]);  // the position stored in the key's low word
-    atomicOr(&kept[t >> 5], 1u << (t & 31));
-  }
-  __syncthreads();
-  // Each thread owns a run of consecutive positions.
+  // prefix is now the C-th largest key.  Each thread owns a run of
+  // consecutive positions.
   const int per = (T + 1023) / 1024;
   const int t0 = tid * per;
   int cnt = 0;
   for (int i = 0; i < per; ++i) {
     const int t = t0 + i;
-    if (t < T && (kept[t >> 5] >> (t & 31)) & 1u) ++cnt;
+    if (t < T && keys[t] >= prefix) ++cnt;
   }
   scan[tid] = cnt;
   __syncthreads();
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(1024) void mod_select_kernel(const float* __restric
   int j = scan[tid] - cnt;
   for (int i = 0; i < per; ++i) {
     const int t = t0 + i;
-    if (t < T && (kept[t >> 5] >> (t & 31)) & 1u) keep[(int64_t)b * C + j++] = b * T + t;
+    if (t < T && keys[t] >= prefix) keep[(int64_t)b * C + j++] = b * T + t;
   }
 }
 

@@ -90,9 +90,9 @@ CASES = [
     ("mod_T128", 512, dict(H=256, Hf=384)),
     ("mod_T100_ragged", 400, dict(H=256, Hf=256)),
     ("mod_T37_odd", 148, dict(H=128, Hf=256, E=8)),
-    # the longest sequence the selection accepts (T = 8192: the sort fills
-    # its whole LDS key array), and T = 5000, which pads 3192 zero keys to
-    # the next power of two
+    # the longest sequence the selection accepts (T = 8192: the keys fill
+    # the whole LDS key array), and T = 5000 (not a power of two; each
+    # thread owns a run of five positions)
     ("mod_T8192_longest", 32768, dict(H=128, Hf=128)),
     ("mod_T5000_padded_sort", 20000, dict(H=128, Hf=128)),
 ]
@@ -109,6 +109,12 @@ def test_mod_parity(cid, S, ov):
 def test_mod_all_kept():
     wl = make_workload("c5", S=256, H=128, Hf=128, E=4, host_weights=True)
     run_and_check(wl, C=wl.cfg["T"])
+
+
+def test_mod_keep_one():
+    # C = 1: the selection descends all eight digit passes to a single key
+    wl = make_workload("c5", S=1024, H=128, Hf=128, E=4, host_weights=True)
+    run_and_check(wl, C=1)
 
 
 def test_mod_zero_scores_keep_first_positions():
