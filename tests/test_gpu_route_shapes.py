@@ -143,6 +143,33 @@ def test_route_tiled(S, H, E, K):
     assert torch.equal(idx, idx2) and torch.equal(gates, gates2) and torch.equal(counts, counts2)
 
 
+def test_route_tiled_parts_no_bias():
+    """The H split with no bias: the part sum adds none (128 tokens x 384
+    experts x H 2048: 8 parts)."""
+    S, H, E, K = 128, 2048, 384, 8
+    print(f"[route tiled, no bias] S={S} H={H} E={E} K={K}", flush=True)
+    sys.stdout.flush()
+    wl = make_workload("c3", S=S, H=H, Hf=128, E=E, K=K, host_weights=False)
+    d = L.dims(S, H, wl.Hf, E, K, "bf16")
+    ws = torch.zeros(L.moe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    x, Wg = to_dev(wl.x, "bf16"), to_dev(wl.Wg, "bf16")
+    logits = torch.empty(S, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
+    gates = torch.empty(S, K, dtype=torch.float32, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    L.moe_clear_status(ws)
+    L.moe_route(d, x, Wg, None, logits, idx, gates, counts, ws)
+    torch.cuda.synchronize()
+    assert L.moe_read_status(ws) == 0
+    got_l = to_host(logits)
+    assert_close("logits", got_l, oracle.router_logits(wl.x, wl.Wg, None), F32_TOL)
+    want_idx = oracle.topk_experts(got_l, K)
+    np.testing.assert_array_equal(to_host(idx), want_idx, err_msg="topk_idx")
+    assert_close("gates", to_host(gates), oracle.gate_weights(got_l, want_idx), F32_TOL)
+    want_counts, _ = oracle.expert_counts(want_idx, E)
+    np.testing.assert_array_equal(to_host(counts), want_counts, err_msg="counts")
+
+
 def test_load_stats():
     """maxvio and load entropy of routing histograms through the C ABI against the oracle."""
     rng = np.random.default_rng(5)
