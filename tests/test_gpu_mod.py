@@ -94,7 +94,7 @@ CASES = [
     # the whole LDS key array), and T = 5000 (not a power of two; each
     # thread owns a run of five positions)
     ("mod_T8192_longest", 32768, dict(H=128, Hf=128)),
-    ("mod_T5000_padded_sort", 20000, dict(H=128, Hf=128)),
+    ("mod_T5000_not_pow2", 20000, dict(H=128, Hf=128)),
 ]
 
 
@@ -115,6 +115,20 @@ def test_mod_keep_one():
     # C = 1: the selection descends all eight digit passes to a single key
     wl = make_workload("c5", S=1024, H=128, Hf=128, E=4, host_weights=True)
     run_and_check(wl, C=1)
+
+
+def test_mod_tied_scores():
+    # scores from three values: the C-th key falls inside a tie group, so the
+    # selection's digit passes descend into the position bits
+    wl = make_workload("c5", S=1024, H=128, Hf=128, E=4, host_weights=True)
+    rng = np.random.default_rng(7)
+    x = np.array(wl.x, dtype=np.float32, copy=True)
+    x[:, 0] = rng.integers(-1, 2, size=x.shape[0]).astype(np.float32)
+    wl.x = x
+    w = np.zeros_like(wl.w_r)
+    w[0] = 1.0
+    wl.w_r = w
+    run_and_check(wl)
 
 
 def test_mod_zero_scores_keep_first_positions():
